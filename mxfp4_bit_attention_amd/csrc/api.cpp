@@ -1,0 +1,275 @@
+// C ABI of libmxattn: argument checks on the host, workspace carving, and
+// dispatch to the HIP kernels.  Every check runs before the first HIP call, so
+// a rejected call touches no device state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "launch.h"
+#include "mxattn.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+int ok() {
+  g_err.clear();
+  return MXATTN_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MXATTN_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t round_up(int64_t n, int64_t m) { return (n + m - 1) / m * m; }
+
+// Largest element count accepted for one tensor (keeps every byte offset and
+// grid size far inside int64 / 31-bit grid limits).
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > limit / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool elems(int64_t a, int64_t b, int64_t c, int64_t d, int64_t* out) {
+  int64_t t;
+  return mul_ok(a, b, kMaxElems, &t) && mul_ok(t, c, kMaxElems, &t) && mul_ok(t, d, kMaxElems, out);
+}
+
+int make_rule(int32_t kind, float qmax, mxattn::Rule* r, const char* who) {
+  float q;
+  if (kind == MXATTN_RULE_UOS) {
+    q = 7.25f;
+  } else if (kind == MXATTN_RULE_OCP) {
+    r->ocp = 1;
+    r->q_exp = 0;
+    r->q_frac = 0;
+    return MXATTN_OK;
+  } else if (kind == MXATTN_RULE_CEIL) {
+    if (!std::isfinite(qmax) || !(qmax > 4.0f) || !(qmax <= 8.0f))
+      return fail(MXATTN_E_INVALID, "%s: ceil rule needs qmax in (4, 8], got %g", who, (double)qmax);
+    q = qmax;
+  } else {
+    return fail(MXATTN_E_INVALID, "%s: unknown rule kind %d", who, (int)kind);
+  }
+  uint32_t b;
+  std::memcpy(&b, &q, 4);
+  r->ocp = 0;
+  r->q_exp = (int)(b >> 23) - 127;
+  r->q_frac = b & 0x7FFFFFu;
+  return MXATTN_OK;
+}
+
+int elem_bytes(int32_t dtype) { return dtype == MXATTN_F32 ? 4 : dtype == MXATTN_BF16 ? 2 : 0; }
+
+float inv_sqrt_f32(int d) { return (float)(1.0 / std::sqrt((double)d)); }
+
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t n) {
+    size_t o = off;
+    off = (off + n + 255) / 256 * 256;
+    return o;
+  }
+};
+
+struct FwdLayout {
+  size_t qc, qs, kc, ks, vc, vs, total;
+};
+
+bool fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, FwdLayout* L) {
+  int64_t nq_e, nkv_e, v_e;
+  const int64_t P = round_up(Nkv, mxattn::kKvTile);
+  if (!elems(B, H, Nq, d, &nq_e) || !elems(B, H, Nkv, d, &nkv_e) || !elems(B, H, P, d, &v_e)) return false;
+  Carve c;
+  L->qc = c.take((size_t)nq_e / 2);
+  L->qs = c.take((size_t)nq_e / 32);
+  L->kc = c.take((size_t)nkv_e / 2);
+  L->ks = c.take((size_t)nkv_e / 32);
+  L->vc = c.take((size_t)v_e / 2);
+  L->vs = c.take((size_t)v_e / 32);
+  L->total = c.off;
+  return true;
+}
+
+int check_attn_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, float softmax_scale,
+                     const char* who) {
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < 1)
+    return fail(MXATTN_E_INVALID, "%s: B, H, Nq, Nkv must be >= 1 (got %lld, %lld, %lld, %lld)", who,
+                (long long)B, (long long)H, (long long)Nq, (long long)Nkv);
+  if (d != 64 && d != 128) return fail(MXATTN_E_UNSUPPORTED, "%s: d must be 64 or 128, got %lld", who, (long long)d);
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
+    return fail(MXATTN_E_INVALID, "%s: softmax_scale must be finite and > 0", who);
+  int64_t t;
+  if (!elems(B, H, Nq > Nkv ? Nq : Nkv, d, &t) || !elems(B, H, round_up(Nkv, mxattn::kKvTile), d, &t))
+    return fail(MXATTN_E_INVALID, "%s: tensor too large", who);
+  if (B * H > 65535) return fail(MXATTN_E_INVALID, "%s: B * H must be <= 65535", who);
+  if (B * H * ((Nq + 127) / 128) > (int64_t)0x7FFFFF00)
+    return fail(MXATTN_E_INVALID, "%s: too many query tiles for one launch", who);
+  return MXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mxattn_kv_tile(void) { return mxattn::kKvTile; }
+
+int64_t mxattn_padded_tokens(int64_t n) { return n < 0 ? -1 : round_up(n, mxattn::kKvTile); }
+
+const char* mxattn_last_error(void) { return g_err.c_str(); }
+
+int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols,
+                    int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
+                    uint8_t* codes, uint8_t* scales, void* stream) {
+  const char* who = "mxattn_quantize";
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MXATTN_E_INVALID, "%s: dtype must be MXATTN_F32 or MXATTN_BF16", who);
+  if (!x || !codes || !scales) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if (batch < 1 || rows < 1 || cols < 1)
+    return fail(MXATTN_E_INVALID, "%s: batch, rows, cols must be >= 1", who);
+  int64_t n;
+  if (!elems(batch, rows, cols, 1, &n)) return fail(MXATTN_E_INVALID, "%s: tensor too large", who);
+  mxattn::Rule rule{};
+  if (int st = make_rule(rule_kind, qmax, &rule, who)) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (axis == MXATTN_AXIS_LAST) {
+    if (cols % 32) return fail(MXATTN_E_INVALID, "%s: cols must be a multiple of 32 for AXIS_LAST", who);
+    if (hadamard) {
+      if (cols != 64 && cols != 128)
+        return fail(MXATTN_E_UNSUPPORTED, "%s: the Hadamard rotation supports cols 64 or 128, got %lld", who,
+                    (long long)cols);
+      e = mxattn::launch_quant_hadamard(x, eb, (int)cols, batch * rows, codes, scales, rule,
+                                        inv_sqrt_f32((int)cols), s);
+    } else {
+      e = mxattn::launch_quant_last(x, eb, n / 32, codes, scales, rule, s);
+    }
+  } else if (axis == MXATTN_AXIS_ROWS) {
+    if (hadamard) return fail(MXATTN_E_INVALID, "%s: AXIS_ROWS does not take a Hadamard rotation", who);
+    if (cols % 2) return fail(MXATTN_E_INVALID, "%s: cols must be even for AXIS_ROWS", who);
+    if (batch > 65535 || (cols + 127) / 128 > 65535)
+      return fail(MXATTN_E_INVALID, "%s: batch and cols/128 must be <= 65535 for AXIS_ROWS", who);
+    const int64_t P = round_up(rows, mxattn::kKvTile);
+    e = mxattn::launch_quant_rows(x, eb, batch, rows, cols, P, codes, scales, rule, s);
+  } else {
+    return fail(MXATTN_E_INVALID, "%s: axis must be MXATTN_AXIS_LAST or MXATTN_AXIS_ROWS", who);
+  }
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nkv < 1 || (d != 64 && d != 128)) return 0;
+  FwdLayout L;
+  if (!fwd_layout(B, H, Nq, Nkv, d, &L)) return 0;
+  return L.total;
+}
+
+static int attention_core(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                          const uint8_t* VTc, const uint8_t* VTs, int64_t B, int64_t H, int64_t Nq,
+                          int64_t Nkv, int64_t d, float softmax_scale, uint32_t pnq,
+                          const mxattn::Rule& pr, void* O, int32_t out_dtype, uint8_t* pc, uint8_t* ps,
+                          hipStream_t s, const char* who) {
+  mxattn::AttnArgs a{};
+  a.qc = Qc;
+  a.qs = Qs;
+  a.kc = Kc;
+  a.ks = Ks;
+  a.vc = VTc;
+  a.vs = VTs;
+  a.o = O;
+  a.pc = pc;
+  a.ps = ps;
+  a.heads = B * H;
+  a.nq = Nq;
+  a.nkv = Nkv;
+  a.kv_pad = round_up(Nkv, mxattn::kKvTile);
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  a.out_bf16 = out_dtype == MXATTN_BF16;
+  hipError_t e = mxattn::launch_attention(a, (int)d, pnq ? 1 : 0, pr, s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+int mxattn_forward_quantized(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
+                             const uint8_t* VTc, const uint8_t* VTs, int64_t B, int64_t H, int64_t Nq,
+                             int64_t Nkv, int64_t d, float softmax_scale, uint32_t pnq,
+                             int32_t p_rule_kind, float p_qmax, void* O, int32_t out_dtype,
+                             uint8_t* p_codes, uint8_t* p_scales, void* stream) {
+  const char* who = "mxattn_forward_quantized";
+  if (!Qc || !Qs || !Kc || !Ks || !VTc || !VTs || !O) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if ((p_codes == nullptr) != (p_scales == nullptr))
+    return fail(MXATTN_E_INVALID, "%s: p_codes and p_scales must both be set or both be NULL", who);
+  if (!aligned16(Qc) || !aligned16(Qs) || !aligned16(Kc) || !aligned16(Ks) || !aligned16(VTc) ||
+      !aligned16(VTs) || !aligned16(O) || (p_codes && (!aligned16(p_codes) || !aligned16(p_scales))))
+    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if (!elem_bytes(out_dtype)) return fail(MXATTN_E_INVALID, "%s: out_dtype must be MXATTN_F32 or MXATTN_BF16", who);
+  if (int st = check_attn_shape(B, H, Nq, Nkv, d, softmax_scale, who)) return st;
+  mxattn::Rule pr{};
+  if (int st = make_rule(p_rule_kind, p_qmax, &pr, who)) return st;
+  return attention_core(Qc, Qs, Kc, Ks, VTc, VTs, B, H, Nq, Nkv, d, softmax_scale, pnq, pr, O, out_dtype,
+                        p_codes, p_scales, static_cast<hipStream_t>(stream), who);
+}
+
+int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nkv, int64_t d, float softmax_scale, uint32_t hadamard,
+                   uint32_t pnq, int32_t rule_kind, float qmax, void* O, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const char* who = "mxattn_forward";
+  const int eb = elem_bytes(dtype);
+  if (!eb) return fail(MXATTN_E_INVALID, "%s: dtype must be MXATTN_F32 or MXATTN_BF16", who);
+  if (!Q || !K || !V || !O || !workspace) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(MXATTN_E_INVALID, "%s: workspace must be 256-byte aligned", who);
+  if (int st = check_attn_shape(B, H, Nq, Nkv, d, softmax_scale, who)) return st;
+  mxattn::Rule rule{};
+  if (int st = make_rule(rule_kind, qmax, &rule, who)) return st;
+  FwdLayout L;
+  if (!fwd_layout(B, H, Nq, Nkv, d, &L)) return fail(MXATTN_E_INVALID, "%s: tensor too large", who);
+  if (workspace_bytes < L.total)
+    return fail(MXATTN_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, workspace_bytes, L.total);
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  uint8_t *qc = w + L.qc, *qs = w + L.qs, *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t P = round_up(Nkv, mxattn::kKvTile);
+  hipError_t e;
+  if (hadamard) {
+    const float c = inv_sqrt_f32((int)d);
+    e = mxattn::launch_quant_hadamard(Q, eb, (int)d, B * H * Nq, qc, qs, rule, c, s);
+    if (e == hipSuccess) e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ks, rule, c, s);
+  } else {
+    e = mxattn::launch_quant_last(Q, eb, B * H * Nq * d / 32, qc, qs, rule, s);
+    if (e == hipSuccess) e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, s);
+  }
+  if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vs, rule, s);
+  if (e != hipSuccess) return hip_fail(e, who);
+  return attention_core(qc, qs, kc, ks, vc, vs, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O, dtype, nullptr,
+                        nullptr, s, who);
+}
+
+}  // extern "C"

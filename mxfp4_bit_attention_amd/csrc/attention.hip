@@ -1,0 +1,386 @@
+// Fused MXFP4 attention forward with Pre-Normalization Quantization (gfx950).
+//
+// Method (Pith review of MXAttention, Figure 4 caption and Core claim; abstract;
+// 10100.com explainer): FlashAttention-2 online softmax where the unnormalised
+// exponential tile P~ = exp(S - m') is quantised to MXFP4 once, and that one
+// quantised tile P^ feeds both the row-sum update and the P^ V update, so the
+// normalised weights sum to one by construction.  With PNQ off the row sum
+// uses the unquantised P~ (the direct placement of Figure 4(C)).
+//
+// Both products are block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4 with
+// fp4 operands and E8M0 scales), computed transposed so that every lane owns
+// one query and one aligned 32-key block:
+//   S^T = K^ Q^^T  : A = 16 keys x 128 d (from LDS), B = Q^ (registers).
+//                    The 16 key rows of MFMA t are keys 32(r/4) + 4t + (r%4),
+//                    r = 0..15, so after the 8 MFMAs of a 128-key tile lane
+//                    l holds S(query l%16, keys 32(l/16) .. 32(l/16)+31).
+//   O^T += V^^T P^^T : A = 16 channels x 128 kv (from LDS), B = P^, which is
+//                    exactly the lane's 32 quantised values plus their E8M0
+//                    scale, so P^ never leaves registers.
+// The row max needs two cross-lane steps (v_permlane16_swap, v_permlane32_swap);
+// the PNQ row sum is one extra MFMA against an all-ones A operand, which sums
+// the same P^ codes the P^ V product uses.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+#include "mx_device.h"
+
+namespace mxattn {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// D = A * B + C with fp4 A and B, E8M0 scales chosen by byte OPA of sa / byte 0 of sb.
+template <int OPA>
+__device__ __forceinline__ v4f mma(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OPA, sa, 0, sb);
+}
+
+__device__ __forceinline__ float xmax4(float x) {
+  // max over lanes l, l^16, l^32, l^48
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float xsum4(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+constexpr int BC = kKvTile;  // 128 keys per kv tile
+
+template <int D>
+struct Lds {
+  static constexpr int KC = BC * D / 2;         // K codes, row = key (D/2 bytes)
+  static constexpr int KS = 512;                // K scales [g][r/4][r%4][t]
+  static constexpr int VC = D * 64;             // V^T codes, row = channel (64 bytes)
+  static constexpr int VS = 512;                // V scales [g][r][ct]
+  static constexpr int STAGE = KC + KS + VC + VS;
+};
+
+// Register staging of one kv tile on its way from HBM to LDS.
+template <int D>
+struct Prefetch {
+  static constexpr int KCH = BC * D / 32 / 256;  // 16-byte K chunks per thread (2 or 1)
+  static constexpr int VCH = D * 4 / 256;        // 16-byte V chunks per thread (2 or 1)
+  uint4 k[KCH];
+  uint4 v[VCH];
+  uint32_t ks;  // this thread's key scales (tid < 128)
+  uint32_t vs;  // this thread's channel scales (tid < D)
+};
+
+template <int D>
+__device__ __forceinline__ void tile_load(Prefetch<D>& pf, const uint8_t* kc, const uint8_t* ks,
+                                          const uint8_t* vc, const uint8_t* vs, int64_t nkv,
+                                          int64_t kv_pad, int j, int tid) {
+  constexpr int KCPR = D / 32;  // 16-byte chunks per K row
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::KCH; ++u) {
+    const int ci = tid + 256 * u;
+    const int kk = ci / KCPR, cc = ci % KCPR;
+    int64_t key = (int64_t)j * BC + kk;
+    key = key < nkv ? key : nkv - 1;
+    pf.k[u] = *reinterpret_cast<const uint4*>(kc + key * (D / 2) + 16 * cc);
+  }
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::VCH; ++u) {
+    const int ci = tid + 256 * u;
+    const int ch = ci / 4, cc = ci % 4;
+    pf.v[u] = *reinterpret_cast<const uint4*>(vc + ch * (kv_pad / 2) + (int64_t)j * 64 + 16 * cc);
+  }
+  pf.ks = 0;
+  pf.vs = 0;
+  if (tid < BC) {
+    int64_t key = (int64_t)j * BC + tid;
+    key = key < nkv ? key : nkv - 1;
+    if constexpr (D == 128)
+      pf.ks = *reinterpret_cast<const uint32_t*>(ks + key * 4);
+    else
+      pf.ks = *reinterpret_cast<const uint16_t*>(ks + key * 2);
+  }
+  if (tid < D) pf.vs = *reinterpret_cast<const uint32_t*>(vs + tid * (kv_pad / 32) + (int64_t)j * 4);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store(const Prefetch<D>& pf, uint8_t* st, int tid) {
+  constexpr int KCPR = D / 32;
+  uint8_t* kc = st;
+  uint8_t* ksc = st + Lds<D>::KC;
+  uint8_t* vc = ksc + Lds<D>::KS;
+  uint8_t* vsc = vc + Lds<D>::VC;
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::KCH; ++u) {
+    const int ci = tid + 256 * u;
+    const int kk = ci / KCPR, cc = ci % KCPR;
+    const int sw = (kk >> 5) & (KCPR - 1);
+    *reinterpret_cast<uint4*>(kc + kk * (D / 2) + 16 * (cc ^ sw)) = pf.k[u];
+  }
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::VCH; ++u) {
+    const int ci = tid + 256 * u;
+    const int ch = ci / 4, cc = ci % 4;
+    *reinterpret_cast<uint4*>(vc + ch * 64 + 16 * (cc ^ ((ch >> 2) & 3))) = pf.v[u];
+  }
+  if (tid < BC) {
+    const int kk = tid;
+#pragma unroll
+    for (int g = 0; g < D / 32; ++g)
+      ksc[((g * 4 + kk / 32) * 4 + kk % 4) * 8 + (kk % 32) / 4] = (uint8_t)(pf.ks >> (8 * g));
+  }
+  if (tid < D) {
+    const int ch = tid;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) vsc[(g * 16 + ch % 16) * 8 + ch / 16] = (uint8_t)(pf.vs >> (8 * g));
+  }
+}
+
+// One workgroup = 4 waves; wave w owns QG groups of 16 queries.
+template <int D, int QG, bool PNQ>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
+  constexpr int NCT = D / 16;  // 16-channel tiles of O
+  constexpr int BR = 64 * QG;  // queries per workgroup
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lds<D>::STAGE];
+
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
+  // consecutive work items (same head, neighbouring query tiles) to the same XCD
+  // and its L2 sees one head's K^/V^ stream at a time.
+  const int bid = blockIdx.x;
+  const int per_xcd = (int)(gridDim.x / 8);
+  const int item = (bid % 8) * per_xcd + bid / 8;
+  if (item >= nblocks) return;
+  const int64_t head = item / qtiles;
+  const int qt = item % qtiles;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15;   // query within a 16-group / row within an MFMA tile
+  const int g = lane >> 4;   // 32-wide k block of the MFMA operand
+
+  const uint8_t* qc = a.qc + head * a.nq * (D / 2);
+  const uint8_t* qs = a.qs + head * a.nq * (D / 32);
+  const uint8_t* kc = a.kc + head * a.nkv * (D / 2);
+  const uint8_t* ks = a.ks + head * a.nkv * (D / 32);
+  const uint8_t* vc = a.vc + head * (int64_t)D * (a.kv_pad / 2);
+  const uint8_t* vs = a.vs + head * (int64_t)D * (a.kv_pad / 32);
+
+  // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop
+  v8i qf[QG];
+  int qsc[QG];
+  int64_t qrow[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    int64_t q = (int64_t)qt * BR + wave * (16 * QG) + qg * 16 + r;
+    qrow[qg] = q;
+    const int64_t qq = q < a.nq ? q : a.nq - 1;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    int sc = 127;
+    if (g < D / 32) {
+      w = *reinterpret_cast<const uint4*>(qc + qq * (D / 2) + 16 * g);
+      sc = qs[qq * (D / 32) + g];
+    }
+    qf[qg] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    qsc[qg] = sc;
+  }
+
+  // ---- online-softmax state
+  v4f acc[QG][NCT];
+  v4f accl[QG];
+  float m[QG], ldir[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    m[qg] = -INFINITY;
+    ldir[qg] = 0.0f;
+    accl[qg] = v4f{0, 0, 0, 0};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] = v4f{0, 0, 0, 0};
+  }
+  const v8i ones = v8i{0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+  const float cl = a.scale_log2;
+  const int ntiles = (int)((a.nkv + BC - 1) / BC);
+
+  Prefetch<D> pf;
+  tile_load<D>(pf, kc, ks, vc, vs, a.nkv, a.kv_pad, 0, tid);
+  tile_store<D>(pf, lds, tid);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    uint8_t* st = lds + (j & 1) * Lds<D>::STAGE;
+    const bool more = j + 1 < ntiles;
+    if (more) tile_load<D>(pf, kc, ks, vc, vs, a.nkv, a.kv_pad, j + 1, tid);
+
+    // ---- K^ and V^ fragments of this tile (shared by the wave's query groups)
+    const uint8_t* lkc = st;
+    const uint8_t* lks = st + Lds<D>::KC;
+    const uint8_t* lvc = lks + Lds<D>::KS;
+    const uint8_t* lvs = lvc + Lds<D>::VC;
+    v8i kf[8];
+    int ksw[2];
+    {
+      const bool live = g < D / 32;
+      const int sw = (r >> 2) & (D / 32 - 1);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int key = 32 * (r >> 2) + 4 * t + (r & 3);
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (live) w = *reinterpret_cast<const uint4*>(lkc + key * (D / 2) + 16 * (g ^ sw));
+        kf[t] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      }
+      uint2 s2 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      if (live) s2 = *reinterpret_cast<const uint2*>(lks + ((g * 4 + (r >> 2)) * 4 + (r & 3)) * 8);
+      ksw[0] = (int)s2.x;
+      ksw[1] = (int)s2.y;
+    }
+    v8i vf[NCT];
+    int vsw[2];
+    {
+      const int sw = (r >> 2) & 3;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int ch = 16 * ct + r;
+        const uint4 w = *reinterpret_cast<const uint4*>(lvc + ch * 64 + 16 * (g ^ sw));
+        vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      }
+      const uint2 s2 = *reinterpret_cast<const uint2*>(lvs + (g * 16 + r) * 8);
+      vsw[0] = (int)s2.x;
+      vsw[1] = (int)s2.y;
+    }
+    const int64_t key0 = (int64_t)j * BC + 32 * g;  // first key of this lane's block
+    const bool tail = (int64_t)(j + 1) * BC > a.nkv;
+
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      // ---- S^T = K^ Q^^T : s[t][jj] = S(query, key0 + 4t + jj)
+      v4f s[8];
+      const v4f z = v4f{0, 0, 0, 0};
+      s[0] = mma<0>(kf[0], qf[qg], z, ksw[0], qsc[qg]);
+      s[1] = mma<1>(kf[1], qf[qg], z, ksw[0], qsc[qg]);
+      s[2] = mma<2>(kf[2], qf[qg], z, ksw[0], qsc[qg]);
+      s[3] = mma<3>(kf[3], qf[qg], z, ksw[0], qsc[qg]);
+      s[4] = mma<0>(kf[4], qf[qg], z, ksw[1], qsc[qg]);
+      s[5] = mma<1>(kf[5], qf[qg], z, ksw[1], qsc[qg]);
+      s[6] = mma<2>(kf[6], qf[qg], z, ksw[1], qsc[qg]);
+      s[7] = mma<3>(kf[7], qf[qg], z, ksw[1], qsc[qg]);
+      if (tail) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (key0 + 4 * t + jj >= a.nkv) s[t][jj] = -INFINITY;
+      }
+      // ---- block max (this lane's 32 keys) and row max (4 lanes)
+      float bm = s[0][0];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) bm = fmaxf(bm, s[t][jj]);
+      const float mnew = fmaxf(m[qg], xmax4(bm));
+      const float alpha = __builtin_amdgcn_exp2f((m[qg] - mnew) * cl);
+      m[qg] = mnew;
+      const float mc = mnew * cl;
+      // ---- P~ = exp(S - m'); its block max is exp(bm - m'), exactly 1 where bm = m'
+      float p[32];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) p[4 * t + jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][jj], cl, -mc));
+      const float pm = __builtin_amdgcn_exp2f((bm - mnew) * cl);
+      // ---- PNQ: quantise P~ once (32-key block, rule prule)
+      const int e = mx_exponent(__float_as_uint(pm), prule);
+      uint32_t pc[4];
+      quant32(p, e, pc);
+      const v8i pf8 = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
+      const int psc = e + 127;
+      if (a.pc != nullptr && qrow[qg] < a.nq) {
+        const int64_t prow = head * a.nq + qrow[qg];
+        *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) = make_uint4(pc[0], pc[1], pc[2], pc[3]);
+        a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)psc;
+      }
+      // ---- rescale the running state when any row's max moved (alpha == 1 is exact)
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] *= alpha;
+        accl[qg] *= alpha;
+        ldir[qg] *= alpha;
+      }
+      // ---- row sum: PNQ sums the same P^ (ones MFMA); direct placement sums P~
+      if constexpr (PNQ) {
+        accl[qg] = mma<0>(ones, pf8, accl[qg], 127, psc);
+      } else {
+        float ls = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) ls += p[k];
+        ldir[qg] += xsum4(ls);
+      }
+      // ---- O~^T += V^^T P^^T
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if ((ct & 3) == 0) acc[qg][ct] = mma<0>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
+        if ((ct & 3) == 1) acc[qg][ct] = mma<1>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
+        if ((ct & 3) == 2) acc[qg][ct] = mma<2>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
+        if ((ct & 3) == 3) acc[qg][ct] = mma<3>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
+      }
+    }
+
+    if (more) tile_store<D>(pf, lds + ((j + 1) & 1) * Lds<D>::STAGE, tid);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O~ / l ; lane holds channels 16ct + 4g + jj of its query
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    if (qrow[qg] >= a.nq) continue;
+    const float l = PNQ ? accl[qg][0] : ldir[qg];
+    const float inv = 1.0f / l;
+    const int64_t orow = head * a.nq + qrow[qg];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int ch = 16 * ct + 4 * g;
+      const float o0 = acc[qg][ct][0] * inv, o1 = acc[qg][ct][1] * inv;
+      const float o2 = acc[qg][ct][2] * inv, o3 = acc[qg][ct][3] * inv;
+      if (a.out_bf16) {
+        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + orow * D + ch;
+        const uint32_t w0 = f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+        const uint32_t w1 = f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+        *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+      } else {
+        float* op = reinterpret_cast<float*>(a.o) + orow * D + ch;
+        *reinterpret_cast<float4*>(op) = make_float4(o0, o1, o2, o3);
+      }
+    }
+  }
+}
+
+template <int D, int QG>
+static hipError_t launch_dq(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) {
+  constexpr int BR = 64 * QG;
+  const int qtiles = (int)((a.nq + BR - 1) / BR);
+  const int64_t nb = (int64_t)qtiles * a.heads;
+  if (nb > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
+  const int nblocks = (int)nb;
+  const unsigned grid = (unsigned)((nblocks + 7) / 8 * 8);
+  if (pnq)
+    hipLaunchKernelGGL((k_attn<D, QG, true>), dim3(grid), dim3(256), 0, s, a, pr, qtiles, nblocks);
+  else
+    hipLaunchKernelGGL((k_attn<D, QG, false>), dim3(grid), dim3(256), 0, s, a, pr, qtiles, nblocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& a, int d, int pnq, Rule p_rule, hipStream_t s) {
+  if (d == 128) return launch_dq<128, 2>(a, pnq, p_rule, s);
+  if (d == 64) return launch_dq<64, 2>(a, pnq, p_rule, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mxattn

@@ -1,0 +1,49 @@
+// Host-side launchers of the HIP kernels (internal to libmxattn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxattn {
+
+// Shared-scale rule in the form the kernels use.  CEIL(q) with q = 1.g * 2^q_exp
+// (UOS is CEIL(7.25)); ocp = 1 selects the floor rule e = floor(log2 M) - 2.
+struct Rule {
+  int ocp;
+  int q_exp;
+  uint32_t q_frac;
+};
+
+// Fused Hadamard + quantise along the last axis; d in {64, 128}; eb = 2 (bf16) or 4 (fp32).
+hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, uint8_t* codes,
+                                 uint8_t* scales, Rule rule, float c, hipStream_t s);
+// Quantise along the last axis in 32-element blocks (nblocks blocks, contiguous).
+hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* codes, uint8_t* scales,
+                             Rule rule, hipStream_t s);
+// Quantise down the rows, transposed output with P (multiple of 128) padded tokens.
+hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
+                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, hipStream_t s);
+
+struct AttnArgs {
+  const uint8_t* qc;
+  const uint8_t* qs;
+  const uint8_t* kc;
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  void* o;
+  uint8_t* pc;   // optional P^ dump
+  uint8_t* ps;
+  int64_t heads;  // B * H
+  int64_t nq;
+  int64_t nkv;
+  int64_t kv_pad;  // P: padded tokens of the transposed V layout
+  float scale_log2;  // softmax_scale * log2(e)
+  int out_bf16;
+};
+
+hipError_t launch_attention(const AttnArgs& a, int d, int pnq, Rule p_rule, hipStream_t s);
+
+constexpr int kKvTile = 128;
+
+}  // namespace mxattn

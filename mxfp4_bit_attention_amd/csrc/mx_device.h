@@ -1,0 +1,89 @@
+// Device-side MXFP4 helpers shared by the quantiser and attention kernels (gfx950).
+//
+// MXFP4 (Pith review of MXAttention, Axiom ledger axiom 1; 10100.com explainer):
+// 32 E2M1 elements share one E8M0 power-of-two scale.  E2M1 rounding here is
+// done by the gfx950 conversion v_cvt_scalef32_pk_fp4_f32, which rounds to
+// nearest even, saturates to +-6, keeps the sign of values that round to zero,
+// and divides by 2^(exponent of its scale operand) exactly before rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace mxattn {
+
+// Shared exponent for a block whose max magnitude has fp32 bit pattern `mbits`
+// (finite, non-negative; zero and subnormals allowed).
+//  CEIL(q): the smallest e with M <= q 2^e.  With M = 1.f 2^E and q = 1.g 2^qe,
+//           that is E - qe when f <= g and E - qe + 1 otherwise.
+//  OCP:     E - 2.
+// M = 0 gives -127; the result is clamped to [-127, 127].
+__device__ __forceinline__ int mx_exponent(uint32_t mbits, Rule r) {
+  if (mbits == 0u) return -127;
+  uint32_t ef = mbits >> 23;
+  int E;
+  uint32_t f;
+  if (ef == 0u) {  // subnormal: M = mbits * 2^-149
+    int lz = __clz(mbits);  // >= 9
+    E = (31 - lz) - 149;
+    f = (mbits << (lz - 8)) & 0x7FFFFFu;
+  } else {
+    E = (int)ef - 127;
+    f = mbits & 0x7FFFFFu;
+  }
+  int e = r.ocp ? (E - 2) : (E - r.q_exp + (f > r.q_frac ? 1 : 0));
+  e = e < -127 ? -127 : e;
+  e = e > 127 ? 127 : e;
+  return e;
+}
+
+// 2^e as an fp32 value (normal range only: -126 <= e <= 127).
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+// Two fp32 values -> one byte of two E2M1 codes (a in the low nibble) written
+// into byte `sel` of `old`, after dividing by 2^e (e the exponent of `scale`).
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_pk_fp4(uint32_t old, float a, float b, float scale) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
+// Quantise 32 fp32 values v[0..31] with shared exponent e into 4 dwords of codes
+// (element k in nibble k of the 16 bytes).  Exact for every e in [-127, 127]:
+// blocks with tiny exponents are first multiplied by 2^64 (exact, since every
+// |v| < 8 * 2^-100 there; it also lifts subnormals into the normal range) and
+// converted with scale 2^(e+64).
+__device__ __forceinline__ void quant32_scaled(const float* v, float s, float pre, uint32_t out[4]) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t r = 0;
+    r = cvt_pk_fp4<0>(r, v[8 * w + 0] * pre, v[8 * w + 1] * pre, s);
+    r = cvt_pk_fp4<1>(r, v[8 * w + 2] * pre, v[8 * w + 3] * pre, s);
+    r = cvt_pk_fp4<2>(r, v[8 * w + 4] * pre, v[8 * w + 5] * pre, s);
+    r = cvt_pk_fp4<3>(r, v[8 * w + 6] * pre, v[8 * w + 7] * pre, s);
+    out[w] = r;
+  }
+}
+
+__device__ __forceinline__ void quant32(const float* v, int e, uint32_t out[4]) {
+  if (__builtin_expect(e >= -100, 1)) {
+    const float s = pow2f(e);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t r = 0;
+      r = cvt_pk_fp4<0>(r, v[8 * w + 0], v[8 * w + 1], s);
+      r = cvt_pk_fp4<1>(r, v[8 * w + 2], v[8 * w + 3], s);
+      r = cvt_pk_fp4<2>(r, v[8 * w + 4], v[8 * w + 5], s);
+      r = cvt_pk_fp4<3>(r, v[8 * w + 6], v[8 * w + 7], s);
+      out[w] = r;
+    }
+  } else {
+    quant32_scaled(v, pow2f(e + 64), 0x1p64f, out);
+  }
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+}  // namespace mxattn
