@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 UOS + PNQ attention pipeline on one MI355X.
+
+One step = the whole hot path on the Wan2.2-720p-shaped self-attention
+(B=1, H=40, N_q=N_kv=75,600, d=128, bf16 inputs resident in HBM): Hadamard +
+UOS quantisation of Q and K along d, UOS quantisation of V along tokens, and
+the fused MXFP4 flash attention with PNQ.  Throughput is 4 B H N_q N_kv d per
+step time, in TFLOP/s.
+
+Printed as one JSON line, with:
+  roofline       the attention kernel (dominant) against the dense MXFP4 MFMA
+                 peak, timed alone with HIP events on its stream, plus HBM
+                 traffic from the committed rocprofv3 counter summary when it
+                 was taken on the current kernel source (else null);
+  quantize_pass  the standalone Hadamard + quantise pass on 40 x 75,600 x 128
+                 bf16 against HBM bandwidth (UOS, OCP and q = 6);
+  cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
+                 on this host, extrapolated to the full workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py --traffic-probe     (one copy of known size + one attention
+                                         launch, for rocprofv3 --pmc runs)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "MXFP4-attn TFLOP/s & % of MXFP4 MFMA peak at H=40,N=75,600,d=128"
+PEAK_MXFP4_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA (published)
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E (published)
+KERNEL_SOURCES = ["mxfp4_bit_attention_amd/csrc/attention.hip", "mxfp4_bit_attention_amd/csrc/mx_device.h",
+                  "mxfp4_bit_attention_amd/csrc/launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wan720p_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_algorithmic_bytes(w) -> int:
+    """Bytes the attention kernel must move once: Q^ and K^ codes + scales, V^T codes +
+    scales (padded to the kv tile), O in bf16."""
+    n_q = w.B * w.H * w.N * w.d
+    pad = -(-w.N // 128) * 128
+    n_v = w.B * w.H * pad * w.d
+    return n_q // 2 + n_q // 32 + n_q // 2 + n_q // 32 + n_v // 2 + n_v // 32 + n_q * 2
+
+
+def quant_algorithmic_bytes(w) -> int:
+    n = w.H * w.N * w.d
+    return n * 2 + n // 2 + n // 32
+
+
+def read_traffic(attn_launch_bytes: int):
+    """HBM bytes per attention launch from the committed counter summary, or None when
+    it is missing or was taken on different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def time_launches(torch, fn, iters: int, stream) -> float:
+    """Average ms per call of fn(), HIP events on `stream` around `iters` back-to-back calls."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(iters):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def cpu_baseline(w) -> dict:
+    """The oracle on head 0: K and V quantisation of the full head, Q quantisation and
+    flash attention for 256 query rows against all N_kv keys; extrapolated."""
+    import numpy as np
+    from oracle import attention as ora
+    from oracle import mxfp4
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing or failing: report the affinity count
+        blas = len(os.sched_getaffinity(0))
+    rows = 256
+    Q = synth.attn_head(w, synth.Q_ID, 0)[:rows]
+    K = synth.attn_head(w, synth.K_ID, 0)
+    V = synth.attn_head(w, synth.V_ID, 0)
+    P = -(-w.N // 128) * 128
+    t = time.perf_counter()
+    Kc, Ks = ora.quantize_qk(K, mxfp4.UOS, True)
+    t_k = time.perf_counter() - t
+    t = time.perf_counter()
+    Vc, Vs = ora.quantize_v(V, mxfp4.UOS, P)
+    t_v = time.perf_counter() - t
+    t = time.perf_counter()
+    Qc, Qs = ora.quantize_qk(Q, mxfp4.UOS, True)
+    t_q = time.perf_counter() - t
+    t = time.perf_counter()
+    ora.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, w.N, float(np.float32(w.softmax_scale)), True, mxfp4.UOS, 128)
+    t_a = time.perf_counter() - t
+    row_blocks = w.N / rows
+    per_head = t_k + t_v + t_q * row_blocks + t_a * row_blocks
+    total = per_head * w.H * w.B
+    return {
+        "value": w.flops / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas),
+        "kind": "oracle",
+        "sample": (f"head 0 of {w.name}: Hadamard+UOS quantise of K ({w.N}x{w.d}) {t_k:.2f}s, token-axis "
+                   f"quantise of V {t_v:.2f}s, Q quantise of {rows} rows {t_q:.3f}s, PNQ flash attention of "
+                   f"{rows} query rows x {w.N} keys {t_a:.2f}s; extrapolated x{row_blocks:.1f} row blocks "
+                   f"x{w.H * w.B} heads to {total:.0f}s for the full step. NumPy elementwise work is "
+                   f"single-threaded; BLAS matmuls used up to {blas} threads; "
+                   f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantize-pass", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path runs on a single MI355X); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-GPU; do not launch it with more than one rank", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp4_bit_attention_amd as mx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WAN_720P
+    scale = float(w.softmax_scale)
+    q = synth.device_attn_tensor(w, synth.Q_ID, dev)
+    k = synth.device_attn_tensor(w, synth.K_ID, dev)
+    v = synth.device_attn_tensor(w, synth.V_ID, dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(mx.mxattn_forward_workspace_bytes(w.B, w.H, w.N, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # attention-only operands (the same kernel mxattn_forward ends with)
+    qc, qs = mx.mxattn_quantize(q.view(-1, w.N, w.d), rule="uos", axis="last", hadamard=True)
+    kc, ks = mx.mxattn_quantize(k.view(-1, w.N, w.d), rule="uos", axis="last", hadamard=True)
+    vc, vs = mx.mxattn_quantize(v.view(-1, w.N, w.d), rule="uos", axis="rows")
+    shp = (w.B, w.H)
+    qc, qs, kc, ks = (t.view(*shp, *t.shape[1:]) for t in (qc, qs, kc, ks))
+    vc, vs = (t.view(*shp, *t.shape[1:]) for t in (vc, vs))
+    out_a = torch.empty_like(q)
+
+    def attn_only():
+        mx.mxattn_forward_quantized(qc, qs, kc, ks, vc, vs, w.N, scale, pnq=True, p_rule="uos", out=out_a)
+
+    if args.traffic_probe:
+        # a plain copy of known size (the counter scale reference), then one attention launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        attn_only()
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_probe": True, "copy_bytes": src.numel(),
+                          "attn_algorithmic_bytes": attn_algorithmic_bytes(w),
+                          "kernel_source_sha256_16": kernel_source_hash()}))
+        return
+
+    def step():
+        mx.mxattn_forward(q, k, v, scale, hadamard=True, pnq=True, rule="uos", out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ms_step = time_launches(torch, step, args.steps, stream)
+    t_wall = (time.perf_counter() - t_wall) / args.steps * 1e3
+    value = w.flops / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel alone, same launch configuration
+    for _ in range(2):
+        attn_only()
+    ms_attn = time_launches(torch, attn_only, args.steps, stream)
+    achieved = w.flops / (ms_attn * 1e-3) / 1e12
+    abytes = attn_algorithmic_bytes(w)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4), "traffic": read_traffic(abytes),
+                "kernel": "k_attn<128,2,PNQ>", "ms_per_launch": round(ms_attn, 3),
+                "algorithmic_bytes": abytes}
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "mxfp4(e2m1+e8m0)->fp32",
+        "data": "synthetic (seeded device generator, outlier-channel Gaussian law)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N_q": w.N, "N_kv": w.N, "d": w.d,
+                   "input_dtype": "bf16", "hadamard": True, "rule": "uos", "pnq": True,
+                   "kv_tile": mx.mxattn_kv_tile()},
+        "pct_of_mxfp4_peak": round(100.0 * value / PEAK_MXFP4_TFLOPS, 2),
+        "wall_ms_per_step": round(t_wall, 3),
+        "roofline": roofline,
+    }
+    del qc, qs, kc, ks, vc, vs
+
+    if not args.no_quantize_pass:
+        qw = synth.QUANT_720P
+        x = synth.device_quant_tensor(qw, dev)
+        qbytes = quant_algorithmic_bytes(qw)
+        c = torch.empty((qw.H, qw.N, qw.d // 2), dtype=torch.uint8, device=dev)
+        s = torch.empty((qw.H, qw.N, qw.d // 32), dtype=torch.uint8, device=dev)
+        qp = {"workload": qw.name, "algorithmic_bytes": qbytes, "peak_GBs": PEAK_HBM_GBS}
+        for name, rule in (("uos", "uos"), ("ocp", "ocp"), ("q6", ("ceil", 6.0))):
+            fn = lambda rule=rule: mx.mxattn_quantize(x, rule=rule, axis="last", hadamard=True, codes=c, scales=s)
+            for _ in range(2):
+                fn()
+            ms = time_launches(torch, fn, max(args.steps, 10), stream)
+            gbs = qbytes / (ms * 1e-3) / 1e9
+            qp[name] = {"us": round(ms * 1e3, 1), "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        result["quantize_pass"] = qp
+        del x, c, s
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -193,3 +193,38 @@ def quant_tensor_bf16(w: QuantWorkload, heads=None, threads: int = 8) -> np.ndar
 def special_values_f32() -> np.ndarray:
     """Every bf16 bit pattern (65,536 values, as fp32) for exhaustive quantiser checks."""
     return bf16_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# Device-side generators with the same laws, for full-size benchmark inputs
+# (hundreds of millions of values).  They draw from torch's seeded device
+# generator, so their values differ from the host generators above; the
+# outlier channels are the same ones the host law picks.
+
+def device_attn_tensor(w: AttnWorkload, tid: int, device="cuda"):
+    import torch
+    g = torch.Generator(device=device).manual_seed(1000 * w.seed + tid)
+    x = torch.randn((w.B, w.H, w.N, w.d), generator=g, device=device, dtype=torch.float32)
+    if tid in (Q_ID, K_ID) and w.outlier_k:
+        for b in range(w.B):
+            for h in range(w.H):
+                ch = torch.from_numpy(outlier_channels(w.seed, tid, b * w.H + h, w.d, w.outlier_k)).to(device)
+                x[b, h][:, ch] *= w.outlier_mult
+    if w.text_rows:
+        t = w.text_rows
+        x[:, :, w.N - t:, :] = torch.randn((w.B, w.H, t, w.d), generator=g, device=device) * w.text_sigma
+    return x.to(torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+
+
+def device_quant_tensor(w: QuantWorkload, device="cuda"):
+    import torch
+    g = torch.Generator(device=device).manual_seed(1000 * w.seed + X_ID)
+    x = torch.randn((w.H, w.N, w.d), generator=g, device=device, dtype=torch.float32)
+    for h in range(w.H):
+        if w.outlier_k:
+            ch = torch.from_numpy(outlier_channels(w.seed, X_ID, h, w.d, w.outlier_k)).to(device)
+            x[h][:, ch] *= w.outlier_mult
+    if w.spike_p > 0:
+        spikes = torch.rand((w.H, w.N, w.d), generator=g, device=device) < w.spike_p
+        x[spikes] *= w.spike_mult
+    return x.to(torch.bfloat16 if w.dtype == "bf16" else torch.float32)
