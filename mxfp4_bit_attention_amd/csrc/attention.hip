@@ -59,57 +59,55 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 constexpr int BC = kKvTile;  // 128 keys per kv tile
+constexpr int NW = 8;        // waves per workgroup (two per SIMD)
+constexpr int NT = 64 * NW;  // threads per workgroup
 
 template <int D>
 struct Lds {
-  static constexpr int KC = BC * D / 2;         // K codes, row = key (D/2 bytes)
+  static constexpr int KC = BC * D / 2;         // K codes, row = key (D/2 bytes), 16-byte units swizzled
   static constexpr int KS = 512;                // K scales [g][r/4][r%4][t]
-  static constexpr int VC = D * 64;             // V^T codes, row = channel (64 bytes)
+  static constexpr int VC = D * 64;             // V^T codes, row = channel (64 bytes), units swizzled
   static constexpr int VS = 512;                // V scales [g][r][ct]
   static constexpr int STAGE = KC + KS + VC + VS;
 };
 
-// Register staging of one kv tile on its way from HBM to LDS.
+// One kv tile in flight from HBM to LDS, held in registers between the two halves.
 template <int D>
 struct Prefetch {
-  static constexpr int KCH = BC * D / 32 / 256;  // 16-byte K chunks per thread (2 or 1)
-  static constexpr int VCH = D * 4 / 256;        // 16-byte V chunks per thread (2 or 1)
-  uint4 k[KCH];
-  uint4 v[VCH];
-  uint32_t ks;  // this thread's key scales (tid < 128)
-  uint32_t vs;  // this thread's channel scales (tid < D)
+  static constexpr int KCHUNKS = BC * D / 32;  // 16-byte chunks of K codes per tile
+  static constexpr int VCHUNKS = D * 4;        // 16-byte chunks of V^T codes per tile
+  uint4 k;
+  uint4 v;
+  uint32_t sc;  // threads [0,128): the key's D/32 scale bytes; [128,128+D): the channel's 4 scale bytes
 };
 
 template <int D>
-__device__ __forceinline__ void tile_load(Prefetch<D>& pf, const uint8_t* kc, const uint8_t* ks,
-                                          const uint8_t* vc, const uint8_t* vs, int64_t nkv,
-                                          int64_t kv_pad, int j, int tid) {
+__device__ __forceinline__ void tile_load(Prefetch<D>& pf, const uint8_t* __restrict__ kc,
+                                          const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc,
+                                          const uint8_t* __restrict__ vs, int nkv, int64_t kv_pad, int j,
+                                          int tid) {
   constexpr int KCPR = D / 32;  // 16-byte chunks per K row
-#pragma unroll
-  for (int u = 0; u < Prefetch<D>::KCH; ++u) {
-    const int ci = tid + 256 * u;
-    const int kk = ci / KCPR, cc = ci % KCPR;
-    int64_t key = (int64_t)j * BC + kk;
+  if (tid < Prefetch<D>::KCHUNKS) {
+    const int kk = tid / KCPR, cc = tid % KCPR;
+    int key = j * BC + kk;
     key = key < nkv ? key : nkv - 1;
-    pf.k[u] = *reinterpret_cast<const uint4*>(kc + key * (D / 2) + 16 * cc);
+    pf.k = *reinterpret_cast<const uint4*>(kc + (int64_t)key * (D / 2) + 16 * cc);
   }
-#pragma unroll
-  for (int u = 0; u < Prefetch<D>::VCH; ++u) {
-    const int ci = tid + 256 * u;
-    const int ch = ci / 4, cc = ci % 4;
-    pf.v[u] = *reinterpret_cast<const uint4*>(vc + ch * (kv_pad / 2) + (int64_t)j * 64 + 16 * cc);
+  if (tid < Prefetch<D>::VCHUNKS) {
+    const int ch = tid / 4, cc = tid % 4;
+    pf.v = *reinterpret_cast<const uint4*>(vc + ch * kv_pad / 2 + j * 64 + 16 * cc);
   }
-  pf.ks = 0;
-  pf.vs = 0;
   if (tid < BC) {
-    int64_t key = (int64_t)j * BC + tid;
+    int key = j * BC + tid;
     key = key < nkv ? key : nkv - 1;
     if constexpr (D == 128)
-      pf.ks = *reinterpret_cast<const uint32_t*>(ks + key * 4);
+      pf.sc = *reinterpret_cast<const uint32_t*>(ks + (int64_t)key * 4);
     else
-      pf.ks = *reinterpret_cast<const uint16_t*>(ks + key * 2);
+      pf.sc = *reinterpret_cast<const uint16_t*>(ks + (int64_t)key * 2);
+  } else if (tid < BC + D) {
+    const int ch = tid - BC;
+    pf.sc = *reinterpret_cast<const uint32_t*>(vs + ch * kv_pad / 32 + j * 4);
   }
-  if (tid < D) pf.vs = *reinterpret_cast<const uint32_t*>(vs + tid * (kv_pad / 32) + (int64_t)j * 4);
 }
 
 template <int D>
@@ -119,37 +117,191 @@ __device__ __forceinline__ void tile_store(const Prefetch<D>& pf, uint8_t* st, i
   uint8_t* ksc = st + Lds<D>::KC;
   uint8_t* vc = ksc + Lds<D>::KS;
   uint8_t* vsc = vc + Lds<D>::VC;
-#pragma unroll
-  for (int u = 0; u < Prefetch<D>::KCH; ++u) {
-    const int ci = tid + 256 * u;
-    const int kk = ci / KCPR, cc = ci % KCPR;
+  if (tid < Prefetch<D>::KCHUNKS) {
+    const int kk = tid / KCPR, cc = tid % KCPR;
     const int sw = (kk >> 5) & (KCPR - 1);
-    *reinterpret_cast<uint4*>(kc + kk * (D / 2) + 16 * (cc ^ sw)) = pf.k[u];
+    *reinterpret_cast<uint4*>(kc + kk * (D / 2) + 16 * (cc ^ sw)) = pf.k;
   }
-#pragma unroll
-  for (int u = 0; u < Prefetch<D>::VCH; ++u) {
-    const int ci = tid + 256 * u;
-    const int ch = ci / 4, cc = ci % 4;
-    *reinterpret_cast<uint4*>(vc + ch * 64 + 16 * (cc ^ ((ch >> 2) & 3))) = pf.v[u];
+  if (tid < Prefetch<D>::VCHUNKS) {
+    const int ch = tid / 4, cc = tid % 4;
+    *reinterpret_cast<uint4*>(vc + ch * 64 + 16 * (cc ^ ((ch >> 2) & 3))) = pf.v;
   }
   if (tid < BC) {
     const int kk = tid;
 #pragma unroll
     for (int g = 0; g < D / 32; ++g)
-      ksc[((g * 4 + kk / 32) * 4 + kk % 4) * 8 + (kk % 32) / 4] = (uint8_t)(pf.ks >> (8 * g));
-  }
-  if (tid < D) {
-    const int ch = tid;
+      ksc[((g * 4 + kk / 32) * 4 + kk % 4) * 8 + (kk % 32) / 4] = (uint8_t)(pf.sc >> (8 * g));
+  } else if (tid < BC + D) {
+    const int ch = tid - BC;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) vsc[(g * 16 + ch % 16) * 8 + ch / 16] = (uint8_t)(pf.vs >> (8 * g));
+    for (int g = 0; g < 4; ++g) vsc[(g * 16 + ch % 16) * 8 + ch / 16] = (uint8_t)(pf.sc >> (8 * g));
   }
 }
 
-// One workgroup = 4 waves; wave w owns QG groups of 16 queries.
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Max of the 32 values s[t][jj] with a max3 tree.
+__device__ __forceinline__ float max32(const v4f (&s)[8]) {
+  float u[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    const int a = 3 * i, b = 3 * i + 1, c = 3 * i + 2;
+    u[i] = fmax3(s[a / 4][a % 4], s[b / 4][b % 4], s[c / 4][c % 4]);
+  }
+  u[10] = fmaxf(s[7][2], s[7][3]);
+  const float w0 = fmax3(u[0], u[1], u[2]), w1 = fmax3(u[3], u[4], u[5]);
+  const float w2 = fmax3(u[6], u[7], u[8]), w3 = fmaxf(u[9], u[10]);
+  return fmaxf(fmax3(w0, w1, w2), w3);
+}
+
+// The shared exponent of a P~ block from its max pm in [0, 1]: every M < 2^-126
+// (including zero and subnormals) gets -127 under any rule with q >= 4, so the
+// biased exponent field alone is enough.
+__device__ __forceinline__ int p_exponent(float pm, Rule r) {
+  const uint32_t b = __float_as_uint(pm);
+  const int E = (int)(b >> 23) - 127;
+  const uint32_t f = b & 0x7FFFFFu;
+  const int e = r.ocp ? E - 2 : E - r.q_exp + (f > r.q_frac ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// One kv tile for one wave's QG query groups.  `rem` (TAIL only) is the number of
+// valid keys in the tile.  Three phases keep the K^ and V^ fragments from being
+// live at the same time: S for every group, then softmax + PNQ per group, then
+// the row-sum and P^ V^ products.
+template <int D, int QG, bool PNQ, bool TAIL>
+__device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int r, int g, int rem,
+                                            const v8i (&qf)[QG], const int (&qsc)[QG],
+                                            v4f (&acc)[QG][D / 16], v4f (&accl)[QG], float (&m)[QG],
+                                            float (&ldir)[QG], float cl, Rule prule, const AttnArgs& a,
+                                            const int64_t (&qrow)[QG], int64_t head, int j) {
+  constexpr int NCT = D / 16;
+  const uint8_t* lkc = st;
+  const uint8_t* lks = st + Lds<D>::KC;
+  const uint8_t* lvc = lks + Lds<D>::KS;
+  const uint8_t* lvs = lvc + Lds<D>::VC;
+  const v4f z = v4f{0, 0, 0, 0};
+
+  // ---- phase 1: S^T = K^ Q^^T.  MFMA t uses keys 32(r/4) + 4t + (r%4) as its 16
+  // rows, so s[qg][t][jj] = S(query, key 32 g + 4 t + jj of this tile).
+  v4f s[QG][8];
+  {
+    v8i kf[8];
+    int ksw[2];
+    const bool live = g < D / 32;
+    const int sw = (r >> 2) & (D / 32 - 1);
+    const uint8_t* kb = lkc + (32 * (r >> 2) + (r & 3)) * (D / 2) + 16 * (g ^ sw);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (live) w = *reinterpret_cast<const uint4*>(kb + 4 * t * (D / 2));
+      kf[t] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    }
+    uint2 s2 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    if (live) s2 = *reinterpret_cast<const uint2*>(lks + ((g * 4 + (r >> 2)) * 4 + (r & 3)) * 8);
+    ksw[0] = (int)s2.x;
+    ksw[1] = (int)s2.y;
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      s[qg][0] = mma<0>(kf[0], qf[qg], z, ksw[0], qsc[qg]);
+      s[qg][1] = mma<1>(kf[1], qf[qg], z, ksw[0], qsc[qg]);
+      s[qg][2] = mma<2>(kf[2], qf[qg], z, ksw[0], qsc[qg]);
+      s[qg][3] = mma<3>(kf[3], qf[qg], z, ksw[0], qsc[qg]);
+      s[qg][4] = mma<0>(kf[4], qf[qg], z, ksw[1], qsc[qg]);
+      s[qg][5] = mma<1>(kf[5], qf[qg], z, ksw[1], qsc[qg]);
+      s[qg][6] = mma<2>(kf[6], qf[qg], z, ksw[1], qsc[qg]);
+      s[qg][7] = mma<3>(kf[7], qf[qg], z, ksw[1], qsc[qg]);
+    }
+  }
+
+  // ---- phase 2: online softmax and PNQ quantisation of P~, per query group
+  v8i pf8[QG];
+  int psc[QG];
+  float alpha[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    if constexpr (TAIL) {
+      const int lim = rem - 32 * g;  // keys of this lane's block that exist
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (4 * t + jj >= lim) s[qg][t][jj] = -INFINITY;
+    }
+    // block max, row max (4 lanes), running max
+    const float bm = max32(s[qg]);
+    const float mnew = fmaxf(m[qg], xmax4(bm));
+    alpha[qg] = __builtin_amdgcn_exp2f((m[qg] - mnew) * cl);
+    m[qg] = mnew;
+    const float mc = mnew * cl;
+    // P~ = exp(S - m'); its block max is exp(bm - m'), exactly 1 where bm = m'
+    float p[32];
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        p[4 * t + jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][t][jj], cl, -mc));
+    const float pm = __builtin_amdgcn_exp2f((bm - mnew) * cl);
+    // PNQ: quantise P~ once, in this lane's aligned 32-key block
+    const int e = p_exponent(pm, prule);
+    uint32_t pc[4];
+    quant32(p, e, pc);
+    pf8[qg] = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
+    psc[qg] = e + 127;
+    if constexpr (!PNQ) {
+      float ls = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) ls += p[k];
+      ldir[qg] = ldir[qg] * alpha[qg] + xsum4(ls);
+    }
+    if (a.pc != nullptr && qrow[qg] < a.nq) {
+      const int64_t prow = head * a.nq + qrow[qg];
+      const int64_t key0 = (int64_t)j * BC + 32 * g;
+      *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) = make_uint4(pc[0], pc[1], pc[2], pc[3]);
+      a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)psc[qg];
+    }
+  }
+
+  // ---- phase 3: rescale, row sum and O~^T += V^^T P^^T
+  v8i vf[NCT];
+  int vsw[2];
+  {
+    const uint8_t* vb = lvc + r * 64 + 16 * (g ^ ((r >> 2) & 3));
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint4 w = *reinterpret_cast<const uint4*>(vb + ct * 16 * 64);
+      vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    }
+    const uint2 s2 = *reinterpret_cast<const uint2*>(lvs + (g * 16 + r) * 8);
+    vsw[0] = (int)s2.x;
+    vsw[1] = (int)s2.y;
+  }
+  const v8i ones = v8i{0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    // rescale the running state when any row's max moved (alpha == 1 is exact)
+    if (__builtin_amdgcn_ballot_w64(alpha[qg] != 1.0f)) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] *= alpha[qg];
+      accl[qg] *= alpha[qg];
+    }
+    // row sum: PNQ sums the same P^ with a ones MFMA (direct placement summed P~ above)
+    if constexpr (PNQ) accl[qg] = mma<0>(ones, pf8[qg], accl[qg], 127, psc[qg]);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      if ((ct & 3) == 0) acc[qg][ct] = mma<0>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
+      if ((ct & 3) == 1) acc[qg][ct] = mma<1>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
+      if ((ct & 3) == 2) acc[qg][ct] = mma<2>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
+      if ((ct & 3) == 3) acc[qg][ct] = mma<3>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
+    }
+  }
+}
+
+// One workgroup = NW waves; wave w owns QG groups of 16 queries.
 template <int D, int QG, bool PNQ>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
+__global__ __launch_bounds__(NT) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   constexpr int NCT = D / 16;  // 16-channel tiles of O
-  constexpr int BR = 64 * QG;  // queries per workgroup
+  constexpr int BR = 16 * QG * NW;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lds<D>::STAGE];
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
@@ -167,6 +319,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, Rule prule, int qtiles
   const int wave = tid >> 6;
   const int r = lane & 15;   // query within a 16-group / row within an MFMA tile
   const int g = lane >> 4;   // 32-wide k block of the MFMA operand
+  const int nkv = (int)a.nkv;
 
   const uint8_t* qc = a.qc + head * a.nq * (D / 2);
   const uint8_t* qs = a.qs + head * a.nq * (D / 32);
@@ -206,135 +359,29 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, Rule prule, int qtiles
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] = v4f{0, 0, 0, 0};
   }
-  const v8i ones = v8i{0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
   const float cl = a.scale_log2;
-  const int ntiles = (int)((a.nkv + BC - 1) / BC);
+  const int ntiles = (nkv + BC - 1) / BC;
+  const int nfull = nkv / BC;  // tiles with no padded key
 
   Prefetch<D> pf;
-  tile_load<D>(pf, kc, ks, vc, vs, a.nkv, a.kv_pad, 0, tid);
+  tile_load<D>(pf, kc, ks, vc, vs, nkv, a.kv_pad, 0, tid);
   tile_store<D>(pf, lds, tid);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    uint8_t* st = lds + (j & 1) * Lds<D>::STAGE;
+  // full tiles; the ragged last tile (if any) is handled after the loop so the
+  // loop body carries no masking
+  for (int j = 0; j < nfull; ++j) {
+    const uint8_t* st = lds + (j & 1) * Lds<D>::STAGE;
     const bool more = j + 1 < ntiles;
-    if (more) tile_load<D>(pf, kc, ks, vc, vs, a.nkv, a.kv_pad, j + 1, tid);
-
-    // ---- K^ and V^ fragments of this tile (shared by the wave's query groups)
-    const uint8_t* lkc = st;
-    const uint8_t* lks = st + Lds<D>::KC;
-    const uint8_t* lvc = lks + Lds<D>::KS;
-    const uint8_t* lvs = lvc + Lds<D>::VC;
-    v8i kf[8];
-    int ksw[2];
-    {
-      const bool live = g < D / 32;
-      const int sw = (r >> 2) & (D / 32 - 1);
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int key = 32 * (r >> 2) + 4 * t + (r & 3);
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (live) w = *reinterpret_cast<const uint4*>(lkc + key * (D / 2) + 16 * (g ^ sw));
-        kf[t] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-      }
-      uint2 s2 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      if (live) s2 = *reinterpret_cast<const uint2*>(lks + ((g * 4 + (r >> 2)) * 4 + (r & 3)) * 8);
-      ksw[0] = (int)s2.x;
-      ksw[1] = (int)s2.y;
-    }
-    v8i vf[NCT];
-    int vsw[2];
-    {
-      const int sw = (r >> 2) & 3;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int ch = 16 * ct + r;
-        const uint4 w = *reinterpret_cast<const uint4*>(lvc + ch * 64 + 16 * (g ^ sw));
-        vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-      }
-      const uint2 s2 = *reinterpret_cast<const uint2*>(lvs + (g * 16 + r) * 8);
-      vsw[0] = (int)s2.x;
-      vsw[1] = (int)s2.y;
-    }
-    const int64_t key0 = (int64_t)j * BC + 32 * g;  // first key of this lane's block
-    const bool tail = (int64_t)(j + 1) * BC > a.nkv;
-
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-      // ---- S^T = K^ Q^^T : s[t][jj] = S(query, key0 + 4t + jj)
-      v4f s[8];
-      const v4f z = v4f{0, 0, 0, 0};
-      s[0] = mma<0>(kf[0], qf[qg], z, ksw[0], qsc[qg]);
-      s[1] = mma<1>(kf[1], qf[qg], z, ksw[0], qsc[qg]);
-      s[2] = mma<2>(kf[2], qf[qg], z, ksw[0], qsc[qg]);
-      s[3] = mma<3>(kf[3], qf[qg], z, ksw[0], qsc[qg]);
-      s[4] = mma<0>(kf[4], qf[qg], z, ksw[1], qsc[qg]);
-      s[5] = mma<1>(kf[5], qf[qg], z, ksw[1], qsc[qg]);
-      s[6] = mma<2>(kf[6], qf[qg], z, ksw[1], qsc[qg]);
-      s[7] = mma<3>(kf[7], qf[qg], z, ksw[1], qsc[qg]);
-      if (tail) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            if (key0 + 4 * t + jj >= a.nkv) s[t][jj] = -INFINITY;
-      }
-      // ---- block max (this lane's 32 keys) and row max (4 lanes)
-      float bm = s[0][0];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) bm = fmaxf(bm, s[t][jj]);
-      const float mnew = fmaxf(m[qg], xmax4(bm));
-      const float alpha = __builtin_amdgcn_exp2f((m[qg] - mnew) * cl);
-      m[qg] = mnew;
-      const float mc = mnew * cl;
-      // ---- P~ = exp(S - m'); its block max is exp(bm - m'), exactly 1 where bm = m'
-      float p[32];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) p[4 * t + jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][jj], cl, -mc));
-      const float pm = __builtin_amdgcn_exp2f((bm - mnew) * cl);
-      // ---- PNQ: quantise P~ once (32-key block, rule prule)
-      const int e = mx_exponent(__float_as_uint(pm), prule);
-      uint32_t pc[4];
-      quant32(p, e, pc);
-      const v8i pf8 = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
-      const int psc = e + 127;
-      if (a.pc != nullptr && qrow[qg] < a.nq) {
-        const int64_t prow = head * a.nq + qrow[qg];
-        *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) = make_uint4(pc[0], pc[1], pc[2], pc[3]);
-        a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)psc;
-      }
-      // ---- rescale the running state when any row's max moved (alpha == 1 is exact)
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] *= alpha;
-        accl[qg] *= alpha;
-        ldir[qg] *= alpha;
-      }
-      // ---- row sum: PNQ sums the same P^ (ones MFMA); direct placement sums P~
-      if constexpr (PNQ) {
-        accl[qg] = mma<0>(ones, pf8, accl[qg], 127, psc);
-      } else {
-        float ls = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 32; ++k) ls += p[k];
-        ldir[qg] += xsum4(ls);
-      }
-      // ---- O~^T += V^^T P^^T
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        if ((ct & 3) == 0) acc[qg][ct] = mma<0>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
-        if ((ct & 3) == 1) acc[qg][ct] = mma<1>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
-        if ((ct & 3) == 2) acc[qg][ct] = mma<2>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
-        if ((ct & 3) == 3) acc[qg][ct] = mma<3>(vf[ct], pf8, acc[qg][ct], vsw[ct >> 2], psc);
-      }
-    }
-
+    if (more) tile_load<D>(pf, kc, ks, vc, vs, nkv, a.kv_pad, j + 1, tid);
+    attend_tile<D, QG, PNQ, false>(st, r, g, BC, qf, qsc, acc, accl, m, ldir, cl, prule, a, qrow, head, j);
     if (more) tile_store<D>(pf, lds + ((j + 1) & 1) * Lds<D>::STAGE, tid);
     __syncthreads();
+  }
+  if (nfull < ntiles) {
+    const int j = nfull;
+    attend_tile<D, QG, PNQ, true>(lds + (j & 1) * Lds<D>::STAGE, r, g, nkv - j * BC, qf, qsc, acc, accl, m,
+                                  ldir, cl, prule, a, qrow, head, j);
   }
 
   // ---- epilogue: O = O~ / l ; lane holds channels 16ct + 4g + jj of its query
@@ -364,16 +411,16 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a, Rule prule, int qtiles
 
 template <int D, int QG>
 static hipError_t launch_dq(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) {
-  constexpr int BR = 64 * QG;
+  constexpr int BR = 16 * QG * NW;
   const int qtiles = (int)((a.nq + BR - 1) / BR);
   const int64_t nb = (int64_t)qtiles * a.heads;
   if (nb > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
   const int nblocks = (int)nb;
   const unsigned grid = (unsigned)((nblocks + 7) / 8 * 8);
   if (pnq)
-    hipLaunchKernelGGL((k_attn<D, QG, true>), dim3(grid), dim3(256), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, QG, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else
-    hipLaunchKernelGGL((k_attn<D, QG, false>), dim3(grid), dim3(256), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, QG, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   return hipGetLastError();
 }
 
