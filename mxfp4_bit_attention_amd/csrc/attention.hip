@@ -30,6 +30,7 @@ namespace mxattn {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
 
 // D = A * B + C with fp4 A and B, E8M0 scales chosen by byte OPA of sa / byte 0 of sb.
 template <int OPA>
@@ -71,13 +72,28 @@ struct Lds {
   static constexpr int STAGE = KC + KS + VC + VS;
 };
 
-// One kv tile in flight from HBM to LDS, held in registers between the two halves.
+// LDS swizzles.  A K^ or V^T row is 64 bytes (4 units of 16 bytes; K^ rows are
+// 32 bytes at D = 64).  A fragment read has 16 lanes reading 16 rows at one unit
+// each; XOR-ing the unit index with these row bits makes every group of 8 lanes
+// hit 8 distinct 16-byte units of a 128-byte line, and every group of 16 lanes 16
+// distinct units of a 256-byte line, so the reads are conflict free whether the
+// LDS serves 8 or 16 lanes of a 128-bit read per cycle.
+template <int D>
+__device__ __forceinline__ int k_swz(int key) {
+  if constexpr (D == 128) return (((key >> 1) ^ (key >> 6)) & 1) | (((key >> 5) & 1) << 1);
+  else return (key >> 5) & 1;
+}
+__device__ __forceinline__ int v_swz(int ch) { return (((ch >> 1) ^ (ch >> 3)) & 1) | (((ch >> 2) & 1) << 1); }
+
+// One kv tile in flight from HBM to LDS, held in registers between the two halves
+// of a loop iteration.  Every thread loads (addresses are clamped into the
+// tensors), so nothing here is conditional and it stays in registers.
 template <int D>
 struct Prefetch {
   static constexpr int KCHUNKS = BC * D / 32;  // 16-byte chunks of K codes per tile
   static constexpr int VCHUNKS = D * 4;        // 16-byte chunks of V^T codes per tile
-  uint4 k;
-  uint4 v;
+  u32x4 k;
+  u32x4 v;
   uint32_t sc;  // threads [0,128): the key's D/32 scale bytes; [128,128+D): the channel's 4 scale bytes
 };
 
@@ -87,25 +103,25 @@ __device__ __forceinline__ void tile_load(Prefetch<D>& pf, const uint8_t* __rest
                                           const uint8_t* __restrict__ vs, int nkv, int64_t kv_pad, int j,
                                           int tid) {
   constexpr int KCPR = D / 32;  // 16-byte chunks per K row
-  if (tid < Prefetch<D>::KCHUNKS) {
-    const int kk = tid / KCPR, cc = tid % KCPR;
-    int key = j * BC + kk;
-    key = key < nkv ? key : nkv - 1;
-    pf.k = *reinterpret_cast<const uint4*>(kc + (int64_t)key * (D / 2) + 16 * cc);
+  {
+    const int ci = tid % Prefetch<D>::KCHUNKS;
+    const int kk = ci / KCPR, cc = ci % KCPR;
+    const int key = min(j * BC + kk, nkv - 1);
+    pf.k = *reinterpret_cast<const u32x4*>(kc + (int64_t)key * (D / 2) + 16 * cc);
   }
-  if (tid < Prefetch<D>::VCHUNKS) {
-    const int ch = tid / 4, cc = tid % 4;
-    pf.v = *reinterpret_cast<const uint4*>(vc + ch * kv_pad / 2 + j * 64 + 16 * cc);
+  {
+    const int ci = tid % Prefetch<D>::VCHUNKS;
+    const int ch = ci / 4, cc = ci % 4;
+    pf.v = *reinterpret_cast<const u32x4*>(vc + ch * kv_pad / 2 + j * 64 + 16 * cc);
   }
   if (tid < BC) {
-    int key = j * BC + tid;
-    key = key < nkv ? key : nkv - 1;
+    const int key = min(j * BC + tid, nkv - 1);
     if constexpr (D == 128)
       pf.sc = *reinterpret_cast<const uint32_t*>(ks + (int64_t)key * 4);
     else
       pf.sc = *reinterpret_cast<const uint16_t*>(ks + (int64_t)key * 2);
-  } else if (tid < BC + D) {
-    const int ch = tid - BC;
+  } else {
+    const int ch = (tid - BC) % D;
     pf.sc = *reinterpret_cast<const uint32_t*>(vs + ch * kv_pad / 32 + j * 4);
   }
 }
@@ -119,12 +135,11 @@ __device__ __forceinline__ void tile_store(const Prefetch<D>& pf, uint8_t* st, i
   uint8_t* vsc = vc + Lds<D>::VC;
   if (tid < Prefetch<D>::KCHUNKS) {
     const int kk = tid / KCPR, cc = tid % KCPR;
-    const int sw = (kk >> 5) & (KCPR - 1);
-    *reinterpret_cast<uint4*>(kc + kk * (D / 2) + 16 * (cc ^ sw)) = pf.k;
+    *reinterpret_cast<u32x4*>(kc + kk * (D / 2) + 16 * (cc ^ k_swz<D>(kk))) = pf.k;
   }
   if (tid < Prefetch<D>::VCHUNKS) {
     const int ch = tid / 4, cc = tid % 4;
-    *reinterpret_cast<uint4*>(vc + ch * 64 + 16 * (cc ^ ((ch >> 2) & 3))) = pf.v;
+    *reinterpret_cast<u32x4*>(vc + ch * 64 + 16 * (cc ^ v_swz(ch))) = pf.v;
   }
   if (tid < BC) {
     const int kk = tid;
@@ -154,22 +169,11 @@ __device__ __forceinline__ float max32(const v4f (&s)[8]) {
   return fmaxf(fmax3(w0, w1, w2), w3);
 }
 
-// The shared exponent of a P~ block from its max pm in [0, 1]: every M < 2^-126
-// (including zero and subnormals) gets -127 under any rule with q >= 4, so the
-// biased exponent field alone is enough.
-__device__ __forceinline__ int p_exponent(float pm, Rule r) {
-  const uint32_t b = __float_as_uint(pm);
-  const int E = (int)(b >> 23) - 127;
-  const uint32_t f = b & 0x7FFFFFu;
-  const int e = r.ocp ? E - 2 : E - r.q_exp + (f > r.q_frac ? 1 : 0);
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
 // One kv tile for one wave's QG query groups.  `rem` (TAIL only) is the number of
 // valid keys in the tile.  Three phases keep the K^ and V^ fragments from being
 // live at the same time: S for every group, then softmax + PNQ per group, then
 // the row-sum and P^ V^ products.
-template <int D, int QG, bool PNQ, bool TAIL>
+template <int D, int QG, bool PNQ, bool DUMP, bool TAIL>
 __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int r, int g, int rem,
                                             const v8i (&qf)[QG], const int (&qsc)[QG],
                                             v4f (&acc)[QG][D / 16], v4f (&accl)[QG], float (&m)[QG],
@@ -189,12 +193,12 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     v8i kf[8];
     int ksw[2];
     const bool live = g < D / 32;
-    const int sw = (r >> 2) & (D / 32 - 1);
-    const uint8_t* kb = lkc + (32 * (r >> 2) + (r & 3)) * (D / 2) + 16 * (g ^ sw);
+    const int key0 = 32 * (r >> 2) + (r & 3);  // the swizzle depends only on key bits 1, 5, 6
+    const uint8_t* kb = lkc + key0 * (D / 2) + 16 * (g ^ k_swz<D>(key0));
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (live) w = *reinterpret_cast<const uint4*>(kb + 4 * t * (D / 2));
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if (live) w = *reinterpret_cast<const u32x4*>(kb + 4 * t * (D / 2));
       kf[t] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
     uint2 s2 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
@@ -243,7 +247,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
         p[4 * t + jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][t][jj], cl, -mc));
     const float pm = __builtin_amdgcn_exp2f((bm - mnew) * cl);
     // PNQ: quantise P~ once, in this lane's aligned 32-key block
-    const int e = p_exponent(pm, prule);
+    const int e = mx_exponent(__float_as_uint(pm), prule);
     uint32_t pc[4];
     quant32(p, e, pc);
     pf8[qg] = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
@@ -254,7 +258,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
       for (int k = 0; k < 32; ++k) ls += p[k];
       ldir[qg] = ldir[qg] * alpha[qg] + xsum4(ls);
     }
-    if (a.pc != nullptr && qrow[qg] < a.nq) {
+    if (DUMP && qrow[qg] < a.nq) {
       const int64_t prow = head * a.nq + qrow[qg];
       const int64_t key0 = (int64_t)j * BC + 32 * g;
       *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) = make_uint4(pc[0], pc[1], pc[2], pc[3]);
@@ -266,10 +270,10 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   v8i vf[NCT];
   int vsw[2];
   {
-    const uint8_t* vb = lvc + r * 64 + 16 * (g ^ ((r >> 2) & 3));
+    const uint8_t* vb = lvc + r * 64 + 16 * (g ^ v_swz(r));  // v_swz(16 ct + r) = v_swz(r)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const uint4 w = *reinterpret_cast<const uint4*>(vb + ct * 16 * 64);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(vb + ct * 16 * 64);
       vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
     const uint2 s2 = *reinterpret_cast<const uint2*>(lvs + (g * 16 + r) * 8);
@@ -298,7 +302,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
 }
 
 // One workgroup = NW waves; wave w owns QG groups of 16 queries.
-template <int D, int QG, bool PNQ>
+template <int D, int QG, bool PNQ, bool DUMP>
 __global__ __launch_bounds__(NT) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   constexpr int NCT = D / 16;  // 16-channel tiles of O
   constexpr int BR = 16 * QG * NW;  // queries per workgroup
@@ -374,13 +378,13 @@ __global__ __launch_bounds__(NT) void k_attn(AttnArgs a, Rule prule, int qtiles,
     const uint8_t* st = lds + (j & 1) * Lds<D>::STAGE;
     const bool more = j + 1 < ntiles;
     if (more) tile_load<D>(pf, kc, ks, vc, vs, nkv, a.kv_pad, j + 1, tid);
-    attend_tile<D, QG, PNQ, false>(st, r, g, BC, qf, qsc, acc, accl, m, ldir, cl, prule, a, qrow, head, j);
+    attend_tile<D, QG, PNQ, DUMP, false>(st, r, g, BC, qf, qsc, acc, accl, m, ldir, cl, prule, a, qrow, head, j);
     if (more) tile_store<D>(pf, lds + ((j + 1) & 1) * Lds<D>::STAGE, tid);
     __syncthreads();
   }
   if (nfull < ntiles) {
     const int j = nfull;
-    attend_tile<D, QG, PNQ, true>(lds + (j & 1) * Lds<D>::STAGE, r, g, nkv - j * BC, qf, qsc, acc, accl, m,
+    attend_tile<D, QG, PNQ, DUMP, true>(lds + (j & 1) * Lds<D>::STAGE, r, g, nkv - j * BC, qf, qsc, acc, accl, m,
                                   ldir, cl, prule, a, qrow, head, j);
   }
 
@@ -417,10 +421,15 @@ static hipError_t launch_dq(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) 
   if (nb > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
   const int nblocks = (int)nb;
   const unsigned grid = (unsigned)((nblocks + 7) / 8 * 8);
-  if (pnq)
-    hipLaunchKernelGGL((k_attn<D, QG, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  const bool dump = a.pc != nullptr;
+  if (pnq && !dump)
+    hipLaunchKernelGGL((k_attn<D, QG, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  else if (pnq && dump)
+    hipLaunchKernelGGL((k_attn<D, QG, true, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  else if (!dump)
+    hipLaunchKernelGGL((k_attn<D, QG, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else
-    hipLaunchKernelGGL((k_attn<D, QG, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, QG, false, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   return hipGetLastError();
 }
 

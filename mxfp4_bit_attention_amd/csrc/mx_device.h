@@ -19,67 +19,40 @@ namespace mxattn {
 //  CEIL(q): the smallest e with M <= q 2^e.  With M = 1.f 2^E and q = 1.g 2^qe,
 //           that is E - qe when f <= g and E - qe + 1 otherwise.
 //  OCP:     E - 2.
-// M = 0 gives -127; the result is clamped to [-127, 127].
+// The result is clamped to [-127, 127].  Every M below 2^-126 (zero and
+// subnormals included) needs e <= -127 under any rule with q >= 4, so reading E
+// from the biased exponent field (E = -127 for those) and clamping is exact.
 __device__ __forceinline__ int mx_exponent(uint32_t mbits, Rule r) {
-  if (mbits == 0u) return -127;
-  uint32_t ef = mbits >> 23;
-  int E;
-  uint32_t f;
-  if (ef == 0u) {  // subnormal: M = mbits * 2^-149
-    int lz = __clz(mbits);  // >= 9
-    E = (31 - lz) - 149;
-    f = (mbits << (lz - 8)) & 0x7FFFFFu;
-  } else {
-    E = (int)ef - 127;
-    f = mbits & 0x7FFFFFu;
-  }
-  int e = r.ocp ? (E - 2) : (E - r.q_exp + (f > r.q_frac ? 1 : 0));
-  e = e < -127 ? -127 : e;
-  e = e > 127 ? 127 : e;
-  return e;
+  const int E = (int)(mbits >> 23) - 127;
+  const uint32_t f = mbits & 0x7FFFFFu;
+  const int e = r.ocp ? (E - 2) : (E - r.q_exp + (f > r.q_frac ? 1 : 0));
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// 2^e as an fp32 value (normal range only: -126 <= e <= 127).
-__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+// The conversion's scale operand for shared exponent e: an fp32 whose exponent
+// field is e + 127 (the instruction uses only that field, as an E8M0 value; the
+// field 0 stands for 2^-127 and subnormal inputs convert exactly).
+__device__ __forceinline__ float e8m0_scale(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
 
 // Two fp32 values -> one byte of two E2M1 codes (a in the low nibble) written
-// into byte `sel` of `old`, after dividing by 2^e (e the exponent of `scale`).
+// into byte `SEL` of `old`, after dividing by 2^e (e from the scale operand).
 template <int SEL>
 __device__ __forceinline__ uint32_t cvt_pk_fp4(uint32_t old, float a, float b, float scale) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
-// Quantise 32 fp32 values v[0..31] with shared exponent e into 4 dwords of codes
-// (element k in nibble k of the 16 bytes).  Exact for every e in [-127, 127]:
-// blocks with tiny exponents are first multiplied by 2^64 (exact, since every
-// |v| < 8 * 2^-100 there; it also lifts subnormals into the normal range) and
-// converted with scale 2^(e+64).
-__device__ __forceinline__ void quant32_scaled(const float* v, float s, float pre, uint32_t out[4]) {
+// Quantise 32 fp32 values v[0..31] with shared exponent e (any e in [-127, 127])
+// into 4 dwords of codes, element k in nibble k of the 16 bytes.
+__device__ __forceinline__ void quant32(const float* v, int e, uint32_t out[4]) {
+  const float s = e8m0_scale(e);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t r = 0;
-    r = cvt_pk_fp4<0>(r, v[8 * w + 0] * pre, v[8 * w + 1] * pre, s);
-    r = cvt_pk_fp4<1>(r, v[8 * w + 2] * pre, v[8 * w + 3] * pre, s);
-    r = cvt_pk_fp4<2>(r, v[8 * w + 4] * pre, v[8 * w + 5] * pre, s);
-    r = cvt_pk_fp4<3>(r, v[8 * w + 6] * pre, v[8 * w + 7] * pre, s);
+    r = cvt_pk_fp4<0>(r, v[8 * w + 0], v[8 * w + 1], s);
+    r = cvt_pk_fp4<1>(r, v[8 * w + 2], v[8 * w + 3], s);
+    r = cvt_pk_fp4<2>(r, v[8 * w + 4], v[8 * w + 5], s);
+    r = cvt_pk_fp4<3>(r, v[8 * w + 6], v[8 * w + 7], s);
     out[w] = r;
-  }
-}
-
-__device__ __forceinline__ void quant32(const float* v, int e, uint32_t out[4]) {
-  if (__builtin_expect(e >= -100, 1)) {
-    const float s = pow2f(e);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t r = 0;
-      r = cvt_pk_fp4<0>(r, v[8 * w + 0], v[8 * w + 1], s);
-      r = cvt_pk_fp4<1>(r, v[8 * w + 2], v[8 * w + 3], s);
-      r = cvt_pk_fp4<2>(r, v[8 * w + 4], v[8 * w + 5], s);
-      r = cvt_pk_fp4<3>(r, v[8 * w + 6], v[8 * w + 7], s);
-      out[w] = r;
-    }
-  } else {
-    quant32_scaled(v, pow2f(e + 64), 0x1p64f, out);
   }
 }
 
