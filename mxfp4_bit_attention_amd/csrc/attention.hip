@@ -60,7 +60,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 constexpr int BC = kKvTile;  // 128 keys per kv tile
-constexpr int NW = 8;        // waves per workgroup (two per SIMD)
+// A workgroup is 4 waves (one per SIMD) and two workgroups share a CU: each SIMD
+// then runs one wave of each, and since the workgroups synchronise on separate
+// barriers they drift out of phase, so one wave's softmax (VALU) overlaps the
+// other's MFMAs.
+constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;  // threads per workgroup
 
 template <int D>
@@ -92,8 +96,10 @@ template <int D>
 struct Prefetch {
   static constexpr int KCHUNKS = BC * D / 32;  // 16-byte chunks of K codes per tile
   static constexpr int VCHUNKS = D * 4;        // 16-byte chunks of V^T codes per tile
-  u32x4 k;
-  u32x4 v;
+  static constexpr int KN = (KCHUNKS + NT - 1) / NT;
+  static constexpr int VN = (VCHUNKS + NT - 1) / NT;
+  u32x4 k[KN];
+  u32x4 v[VN];
   uint32_t sc;  // threads [0,128): the key's D/32 scale bytes; [128,128+D): the channel's 4 scale bytes
 };
 
@@ -103,16 +109,18 @@ __device__ __forceinline__ void tile_load(Prefetch<D>& pf, const uint8_t* __rest
                                           const uint8_t* __restrict__ vs, int nkv, int64_t kv_pad, int j,
                                           int tid) {
   constexpr int KCPR = D / 32;  // 16-byte chunks per K row
-  {
-    const int ci = tid % Prefetch<D>::KCHUNKS;
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::KN; ++u) {
+    const int ci = (tid + NT * u) % Prefetch<D>::KCHUNKS;
     const int kk = ci / KCPR, cc = ci % KCPR;
     const int key = min(j * BC + kk, nkv - 1);
-    pf.k = *reinterpret_cast<const u32x4*>(kc + (int64_t)key * (D / 2) + 16 * cc);
+    pf.k[u] = *reinterpret_cast<const u32x4*>(kc + (int64_t)key * (D / 2) + 16 * cc);
   }
-  {
-    const int ci = tid % Prefetch<D>::VCHUNKS;
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::VN; ++u) {
+    const int ci = (tid + NT * u) % Prefetch<D>::VCHUNKS;
     const int ch = ci / 4, cc = ci % 4;
-    pf.v = *reinterpret_cast<const u32x4*>(vc + ch * kv_pad / 2 + j * 64 + 16 * cc);
+    pf.v[u] = *reinterpret_cast<const u32x4*>(vc + ch * kv_pad / 2 + j * 64 + 16 * cc);
   }
   if (tid < BC) {
     const int key = min(j * BC + tid, nkv - 1);
@@ -133,13 +141,21 @@ __device__ __forceinline__ void tile_store(const Prefetch<D>& pf, uint8_t* st, i
   uint8_t* ksc = st + Lds<D>::KC;
   uint8_t* vc = ksc + Lds<D>::KS;
   uint8_t* vsc = vc + Lds<D>::VC;
-  if (tid < Prefetch<D>::KCHUNKS) {
-    const int kk = tid / KCPR, cc = tid % KCPR;
-    *reinterpret_cast<u32x4*>(kc + kk * (D / 2) + 16 * (cc ^ k_swz<D>(kk))) = pf.k;
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::KN; ++u) {
+    const int ci = tid + NT * u;
+    if (ci < Prefetch<D>::KCHUNKS) {
+      const int kk = ci / KCPR, cc = ci % KCPR;
+      *reinterpret_cast<u32x4*>(kc + kk * (D / 2) + 16 * (cc ^ k_swz<D>(kk))) = pf.k[u];
+    }
   }
-  if (tid < Prefetch<D>::VCHUNKS) {
-    const int ch = tid / 4, cc = tid % 4;
-    *reinterpret_cast<u32x4*>(vc + ch * 64 + 16 * (cc ^ v_swz(ch))) = pf.v;
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::VN; ++u) {
+    const int ci = tid + NT * u;
+    if (ci < Prefetch<D>::VCHUNKS) {
+      const int ch = ci / 4, cc = ci % 4;
+      *reinterpret_cast<u32x4*>(vc + ch * 64 + 16 * (cc ^ v_swz(ch))) = pf.v[u];
+    }
   }
   if (tid < BC) {
     const int kk = tid;
@@ -303,7 +319,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
 
 // One workgroup = NW waves; wave w owns QG groups of 16 queries.
 template <int D, int QG, bool PNQ, bool DUMP>
-__global__ __launch_bounds__(NT) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
+__global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   constexpr int NCT = D / 16;  // 16-channel tiles of O
   constexpr int BR = 16 * QG * NW;  // queries per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lds<D>::STAGE];
