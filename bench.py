@@ -93,7 +93,8 @@ def time_launches(torch, fn, iters: int, stream) -> float:
 
 def cpu_baseline(w) -> dict:
     """The oracle on head 0: K and V quantisation of the full head, Q quantisation and
-    flash attention for 256 query rows against all N_kv keys; extrapolated."""
+    flash attention for 1024 query rows against all N_kv keys (about 10 s of CPU work);
+    extrapolated to every row block and head."""
     import numpy as np
     from oracle import attention as ora
     from oracle import mxfp4
@@ -102,7 +103,7 @@ def cpu_baseline(w) -> dict:
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing or failing: report the affinity count
         blas = len(os.sched_getaffinity(0))
-    rows = 256
+    rows = 1024
     Q = synth.attn_head(w, synth.Q_ID, 0)[:rows]
     K = synth.attn_head(w, synth.K_ID, 0)
     V = synth.attn_head(w, synth.V_ID, 0)

@@ -47,7 +47,9 @@ __device__ __forceinline__ void quant32(const float* v, int e, uint32_t out[4]) 
   const float s = e8m0_scale(e);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint32_t r = 0;
+    // all four bytes of r are written below, so its initial value is irrelevant:
+    // start from a value that is dead afterwards instead of materialising a zero
+    uint32_t r = __float_as_uint(v[8 * w + 0]);
     r = cvt_pk_fp4<0>(r, v[8 * w + 0], v[8 * w + 1], s);
     r = cvt_pk_fp4<1>(r, v[8 * w + 2], v[8 * w + 3], s);
     r = cvt_pk_fp4<2>(r, v[8 * w + 4], v[8 * w + 5], s);
