@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 #include "mx_device.h"
 
@@ -90,8 +92,9 @@ __device__ __forceinline__ int k_swz(int key) {
 __device__ __forceinline__ int v_swz(int ch) { return (((ch >> 1) ^ (ch >> 3)) & 1) | (((ch >> 2) & 1) << 1); }
 
 // One kv tile in flight from HBM to LDS, held in registers between the two halves
-// of a loop iteration.  Every thread loads (addresses are clamped into the
-// tensors), so nothing here is conditional and it stays in registers.
+// of a loop iteration.  The loads use buffer descriptors rebuilt per tile on the
+// scalar unit (base advanced to the tile, size = bytes left), with per-thread
+// offsets that do not change across tiles; reads past the last key return zero.
 template <int D>
 struct Prefetch {
   static constexpr int KCHUNKS = BC * D / 32;  // 16-byte chunks of K codes per tile
@@ -103,34 +106,60 @@ struct Prefetch {
   uint32_t sc;  // threads [0,128): the key's D/32 scale bytes; [128,128+D): the channel's 4 scale bytes
 };
 
+// Per-thread byte offsets of the tile loads (tile independent).
 template <int D>
-__device__ __forceinline__ void tile_load(Prefetch<D>& pf, const uint8_t* __restrict__ kc,
-                                          const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc,
-                                          const uint8_t* __restrict__ vs, int nkv, int64_t kv_pad, int j,
-                                          int tid) {
+struct LoadOffsets {
+  uint32_t k[Prefetch<D>::KN];
+  uint32_t v[Prefetch<D>::VN];
+  uint32_t sc;
+};
+
+template <int D>
+__device__ __forceinline__ LoadOffsets<D> load_offsets(int64_t kv_pad, int tid) {
   constexpr int KCPR = D / 32;  // 16-byte chunks per K row
+  LoadOffsets<D> o;
 #pragma unroll
   for (int u = 0; u < Prefetch<D>::KN; ++u) {
     const int ci = (tid + NT * u) % Prefetch<D>::KCHUNKS;
-    const int kk = ci / KCPR, cc = ci % KCPR;
-    const int key = min(j * BC + kk, nkv - 1);
-    pf.k[u] = *reinterpret_cast<const u32x4*>(kc + (int64_t)key * (D / 2) + 16 * cc);
+    o.k[u] = (uint32_t)((ci / KCPR) * (D / 2) + 16 * (ci % KCPR));
   }
 #pragma unroll
   for (int u = 0; u < Prefetch<D>::VN; ++u) {
     const int ci = (tid + NT * u) % Prefetch<D>::VCHUNKS;
-    const int ch = ci / 4, cc = ci % 4;
-    pf.v[u] = *reinterpret_cast<const u32x4*>(vc + ch * kv_pad / 2 + j * 64 + 16 * cc);
+    o.v[u] = (uint32_t)((ci / 4) * (kv_pad / 2) + 16 * (ci % 4));
   }
-  if (tid < BC) {
-    const int key = min(j * BC + tid, nkv - 1);
+  o.sc = tid < BC ? (uint32_t)(tid * (D / 32)) : (uint32_t)(((tid - BC) % D) * (kv_pad / 32));
+  return o;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
+}
+
+template <int D>
+__device__ __forceinline__ void tile_load(Prefetch<D>& pf, const LoadOffsets<D>& o, const uint8_t* kc,
+                                          const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int nkv,
+                                          int64_t kv_pad, int j, int tid) {
+  const int64_t k0 = (int64_t)j * BC;  // first key of the tile
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kc + k0 * (D / 2), (nkv - k0) * (D / 2));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vc + j * 64, (int64_t)D * kv_pad / 2 - j * 64);
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::KN; ++u) pf.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k[u], 0, 0);
+#pragma unroll
+  for (int u = 0; u < Prefetch<D>::VN; ++u) pf.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v[u], 0, 0);
+  // waves 0-1 (threads < 128) load key scales, waves 2-3 channel scales: the branch is
+  // wave-uniform, so each load sees one scalar descriptor
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (wave < BC / 64) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(ks + k0 * (D / 32), (nkv - k0) * (D / 32));
     if constexpr (D == 128)
-      pf.sc = *reinterpret_cast<const uint32_t*>(ks + (int64_t)key * 4);
+      pf.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, o.sc, 0, 0);
     else
-      pf.sc = *reinterpret_cast<const uint16_t*>(ks + (int64_t)key * 2);
+      pf.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, o.sc, 0, 0);
   } else {
-    const int ch = (tid - BC) % D;
-    pf.sc = *reinterpret_cast<const uint32_t*>(vs + ch * kv_pad / 32 + j * 4);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(vs + j * 4, (int64_t)D * kv_pad / 32 - j * 4);
+    pf.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, o.sc, 0, 0);
   }
 }
 
@@ -194,7 +223,8 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
                                             const v8i (&qf)[QG], const int (&qsc)[QG],
                                             v4f (&acc)[QG][D / 16], v4f (&accl)[QG], float (&m)[QG],
                                             float (&ldir)[QG], float cl, Rule prule, const AttnArgs& a,
-                                            const int64_t (&qrow)[QG], int64_t head, int j) {
+                                            const int64_t (&qrow)[QG], int64_t head, int j,
+                                            const uint8_t* lones) {
   constexpr int NCT = D / 16;
   const uint8_t* lkc = st;
   const uint8_t* lks = st + Lds<D>::KC;
@@ -296,7 +326,13 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     vsw[0] = (int)s2.x;
     vsw[1] = (int)s2.y;
   }
-  const v8i ones = v8i{0x22222222, 0x22222222, 0x22222222, 0x22222222, 0, 0, 0, 0};
+  v8i ones;
+  {
+    // all-ones fp4 operand (code 0x2 = 1.0) for the PNQ row sum, read from LDS so it
+    // does not occupy registers outside this phase
+    const u32x4 w = *reinterpret_cast<const u32x4*>(lones);
+    ones = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  }
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     // rescale the running state when any row's max moved (alpha == 1 is exact)
@@ -322,7 +358,8 @@ template <int D, int QG, bool PNQ, bool DUMP>
 __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   constexpr int NCT = D / 16;  // 16-channel tiles of O
   constexpr int BR = 16 * QG * NW;  // queries per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lds<D>::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lds<D>::STAGE + 16];
+  uint8_t* const lones = lds + 2 * Lds<D>::STAGE;
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
   // consecutive work items (same head, neighbouring query tiles) to the same XCD
@@ -383,25 +420,37 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
   const int ntiles = (nkv + BC - 1) / BC;
   const int nfull = nkv / BC;  // tiles with no padded key
 
+  const LoadOffsets<D> lo = load_offsets<D>(a.kv_pad, tid);
   Prefetch<D> pf;
-  tile_load<D>(pf, kc, ks, vc, vs, nkv, a.kv_pad, 0, tid);
+  tile_load<D>(pf, lo, kc, ks, vc, vs, nkv, a.kv_pad, 0, tid);
   tile_store<D>(pf, lds, tid);
+  if (tid == 0) *reinterpret_cast<uint4*>(lones) = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
   __syncthreads();
 
-  // full tiles; the ragged last tile (if any) is handled after the loop so the
-  // loop body carries no masking
-  for (int j = 0; j < nfull; ++j) {
-    const uint8_t* st = lds + (j & 1) * Lds<D>::STAGE;
+  // One loop iteration on tile j held in LDS stage S, prefetching tile j+1 into the
+  // other stage.  Full tiles only; the ragged last tile is handled after the loop,
+  // so the loop body carries no masking.
+  auto full_tile = [&](int j, auto stage) {
+    constexpr int S = decltype(stage)::value;
     const bool more = j + 1 < ntiles;
-    if (more) tile_load<D>(pf, kc, ks, vc, vs, nkv, a.kv_pad, j + 1, tid);
-    attend_tile<D, QG, PNQ, DUMP, false>(st, r, g, BC, qf, qsc, acc, accl, m, ldir, cl, prule, a, qrow, head, j);
-    if (more) tile_store<D>(pf, lds + ((j + 1) & 1) * Lds<D>::STAGE, tid);
+    if (more) tile_load<D>(pf, lo, kc, ks, vc, vs, nkv, a.kv_pad, j + 1, tid);
+    attend_tile<D, QG, PNQ, DUMP, false>(lds + S * Lds<D>::STAGE, r, g, BC, qf, qsc, acc, accl, m, ldir, cl,
+                                         prule, a, qrow, head, j, lones);
+    if (more) tile_store<D>(pf, lds + (1 - S) * Lds<D>::STAGE, tid);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    full_tile(j, std::integral_constant<int, 0>{});
+    full_tile(j + 1, std::integral_constant<int, 1>{});
   }
-  if (nfull < ntiles) {
-    const int j = nfull;
-    attend_tile<D, QG, PNQ, DUMP, true>(lds + (j & 1) * Lds<D>::STAGE, r, g, nkv - j * BC, qf, qsc, acc, accl, m,
-                                  ldir, cl, prule, a, qrow, head, j);
+  if (j < nfull) {
+    full_tile(j, std::integral_constant<int, 0>{});
+    ++j;
+  }
+  if (j < ntiles) {
+    attend_tile<D, QG, PNQ, DUMP, true>(lds + (j & 1) * Lds<D>::STAGE, r, g, nkv - j * BC, qf, qsc, acc, accl,
+                                        m, ldir, cl, prule, a, qrow, head, j, lones);
   }
 
   // ---- epilogue: O = O~ / l ; lane holds channels 16ct + 4g + jj of its query
