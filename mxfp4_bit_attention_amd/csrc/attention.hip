@@ -64,71 +64,74 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 constexpr int BC = kKvTile;  // 128 keys per kv tile
 // A workgroup is 4 waves (one per SIMD) and two workgroups share a CU: each SIMD
 // then runs one wave of each, and since the workgroups synchronise on separate
-// barriers they drift out of phase, so one wave's softmax (VALU) overlaps the
-// other's MFMAs.
+// barriers they drift out of phase, so one wave's softmax overlaps the other's MFMAs.
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;  // threads per workgroup
 
+// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding: vmcnt low
+// bits [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define MX_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 0xF) | (((n) >> 4) << 14)) | (0x7 << 4) | (0xF << 8))
+
+// One kv tile in LDS.  Every region is filled by global->LDS DMA, where lane L of a
+// wave writes 16 (or 4) bytes at base + 16 L (or 4 L); the layouts below are chosen
+// so that each MFMA fragment is one contiguous 1 KB read per wave.
+//  K codes  [t][g][r] 16-byte units: unit (t, g, r) = d-block g of key kappa(t, r)
+//  K scales [8 r + t] dwords: the D/32 scale bytes of key kappa(t, r)
+//  V codes  [ct][g][r]: unit (ct, g, r) = keys 32 g .. 32 g + 31 of channel 16 ct + r
+//  V scales [NCT r + ct] dwords: the 4 scale bytes (one per 32-key block) of channel 16 ct + r
 template <int D>
-struct Lds {
-  static constexpr int KC = BC * D / 2;         // K codes, row = key (D/2 bytes), 16-byte units swizzled
-  static constexpr int KS = 512;                // K scales [g][r/4][r%4][t]
-  static constexpr int VC = D * 64;             // V^T codes, row = channel (64 bytes), units swizzled
-  static constexpr int VS = 512;                // V scales [g][r][ct]
+struct Geo {
+  static constexpr int NCT = D / 16;        // 16-channel tiles of O
+  static constexpr int GK = D / 32;         // 32-element blocks per key row
+  static constexpr int KC = BC * D / 2;
+  static constexpr int KS = 4 * BC;
+  static constexpr int VC = D * BC / 2;
+  static constexpr int VS = 4 * D;
+  static constexpr int OFF_KS = KC;
+  static constexpr int OFF_VC = KC + KS;
+  static constexpr int OFF_VS = KC + KS + VC;
   static constexpr int STAGE = KC + KS + VC + VS;
+  static constexpr int CODE_DMA = D / 64;       // 1 KB code loads per wave per tile, for K and for V
+  static constexpr int NDMA = 2 * CODE_DMA + 1;  // DMA instructions per wave per tile
+  static_assert(KC == NW * CODE_DMA * 1024 && VC == NW * CODE_DMA * 1024, "code DMA split");
 };
 
-// LDS swizzles.  A K^ or V^T row is 64 bytes (4 units of 16 bytes; K^ rows are
-// 32 bytes at D = 64).  A fragment read has 16 lanes reading 16 rows at one unit
-// each; XOR-ing the unit index with these row bits makes every group of 8 lanes
-// hit 8 distinct 16-byte units of a 128-byte line, and every group of 16 lanes 16
-// distinct units of a 256-byte line, so the reads are conflict free whether the
-// LDS serves 8 or 16 lanes of a 128-bit read per cycle.
-template <int D>
-__device__ __forceinline__ int k_swz(int key) {
-  if constexpr (D == 128) return (((key >> 1) ^ (key >> 6)) & 1) | (((key >> 5) & 1) << 1);
-  else return (key >> 5) & 1;
-}
-__device__ __forceinline__ int v_swz(int ch) { return (((ch >> 1) ^ (ch >> 3)) & 1) | (((ch >> 2) & 1) << 1); }
+// The 16 keys of S^T MFMA t (t = 0..7): row r holds key 32(r/4) + 4t + (r%4), so the
+// output lane (query, g) ends up with keys 32g .. 32g + 31 of the tile.
+__device__ __forceinline__ int kappa(int t, int r) { return 32 * (r >> 2) + 4 * t + (r & 3); }
 
-// One kv tile in flight from HBM to LDS, held in registers between the two halves
-// of a loop iteration.  The loads use buffer descriptors rebuilt per tile on the
-// scalar unit (base advanced to the tile, size = bytes left), with per-thread
-// offsets that do not change across tiles; reads past the last key return zero.
+// Per-lane byte offsets of a wave's tile DMAs (the same for every tile).
 template <int D>
-struct Prefetch {
-  static constexpr int KCHUNKS = BC * D / 32;  // 16-byte chunks of K codes per tile
-  static constexpr int VCHUNKS = D * 4;        // 16-byte chunks of V^T codes per tile
-  static constexpr int KN = (KCHUNKS + NT - 1) / NT;
-  static constexpr int VN = (VCHUNKS + NT - 1) / NT;
-  u32x4 k[KN];
-  u32x4 v[VN];
-  uint32_t sc;  // threads [0,128): the key's D/32 scale bytes; [128,128+D): the channel's 4 scale bytes
-};
-
-// Per-thread byte offsets of the tile loads (tile independent).
-template <int D>
-struct LoadOffsets {
-  uint32_t k[Prefetch<D>::KN];
-  uint32_t v[Prefetch<D>::VN];
-  uint32_t sc;
+struct DmaOffsets {
+  uint32_t k[Geo<D>::CODE_DMA];
+  uint32_t v[Geo<D>::CODE_DMA];
+  uint32_t s;  // waves 0-1: key scales; waves 2-3: channel scales
 };
 
 template <int D>
-__device__ __forceinline__ LoadOffsets<D> load_offsets(int64_t kv_pad, int tid) {
-  constexpr int KCPR = D / 32;  // 16-byte chunks per K row
-  LoadOffsets<D> o;
+__device__ __forceinline__ DmaOffsets<D> dma_offsets(int64_t kv_pad, int wave, int lane) {
+  using G = Geo<D>;
+  DmaOffsets<D> o;
 #pragma unroll
-  for (int u = 0; u < Prefetch<D>::KN; ++u) {
-    const int ci = (tid + NT * u) % Prefetch<D>::KCHUNKS;
-    o.k[u] = (uint32_t)((ci / KCPR) * (D / 2) + 16 * (ci % KCPR));
+  for (int u = 0; u < G::CODE_DMA; ++u) {
+    const int s = 64 * (G::CODE_DMA * wave + u) + lane;  // 16-byte unit of the K region
+    const int t = s / (16 * G::GK), g = (s / 16) % G::GK, r = s % 16;
+    o.k[u] = (uint32_t)(kappa(t, r) * (D / 2) + 16 * g);
   }
 #pragma unroll
-  for (int u = 0; u < Prefetch<D>::VN; ++u) {
-    const int ci = (tid + NT * u) % Prefetch<D>::VCHUNKS;
-    o.v[u] = (uint32_t)((ci / 4) * (kv_pad / 2) + 16 * (ci % 4));
+  for (int u = 0; u < G::CODE_DMA; ++u) {
+    const int s = 64 * (G::CODE_DMA * wave + u) + lane;  // 16-byte unit of the V region
+    const int ct = s / 64, g = (s / 16) % 4, r = s % 16;
+    o.v[u] = (uint32_t)((16 * ct + r) * (kv_pad / 2) + 16 * g);
   }
-  o.sc = tid < BC ? (uint32_t)(tid * (D / 32)) : (uint32_t)(((tid - BC) % D) * (kv_pad / 32));
+  if (wave < 2) {
+    const int p = 64 * wave + lane;  // dword 8 r + t of the K scale region
+    o.s = (uint32_t)(kappa(p % 8, p / 8) * (D / 32));
+  } else {
+    const int p = (wave - 2) * (D / 2) + lane;  // dword NCT r + ct of the V scale region
+    const int ch = 16 * (p % G::NCT) + p / G::NCT;
+    o.s = (uint32_t)(ch * (kv_pad / 32));
+  }
   return o;
 }
 
@@ -137,65 +140,62 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int6
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global->LDS DMA of 16, 4 or 2 bytes per lane: lane L writes at lds + 16 L (the 4- and
+// 2-byte forms at lds + 4 L, zero-extended); `lds` must be the same in every lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 2, off, 0, 0, 0);
+}
+
+// Issue the DMAs of tile j into stage `st`: NDMA instructions per wave.  Buffer
+// descriptors are rebuilt per tile on the scalar unit (base at the tile, size = bytes
+// left), so keys past the last one, and whole tiles past the end, read as zero
+// without touching memory.
 template <int D>
-__device__ __forceinline__ void tile_load(Prefetch<D>& pf, const LoadOffsets<D>& o, const uint8_t* kc,
-                                          const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int nkv,
-                                          int64_t kv_pad, int j, int tid) {
-  const int64_t k0 = (int64_t)j * BC;  // first key of the tile
-  const __amdgpu_buffer_rsrc_t rk = rsrc(kc + k0 * (D / 2), (nkv - k0) * (D / 2));
-  const __amdgpu_buffer_rsrc_t rv = rsrc(vc + j * 64, (int64_t)D * kv_pad / 2 - j * 64);
+__device__ __forceinline__ void tile_dma(uint8_t* st, const DmaOffsets<D>& o, const uint8_t* kc,
+                                         const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int nkv,
+                                         int64_t kv_pad, int j, int ntiles, int wave, int lane) {
+  using G = Geo<D>;
+  const bool live = j < ntiles;
+  const int64_t k0 = (int64_t)j * BC;
+  const __amdgpu_buffer_rsrc_t rk = rsrc(kc + k0 * (D / 2), live ? (nkv - k0) * (D / 2) : 0);
+  const __amdgpu_buffer_rsrc_t rv = rsrc(vc + (int64_t)j * 64, live ? (int64_t)D * kv_pad / 2 - (int64_t)j * 64 : 0);
 #pragma unroll
-  for (int u = 0; u < Prefetch<D>::KN; ++u) pf.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, o.k[u], 0, 0);
+  for (int u = 0; u < G::CODE_DMA; ++u) dma16(rk, st + 1024 * (G::CODE_DMA * wave + u), o.k[u]);
 #pragma unroll
-  for (int u = 0; u < Prefetch<D>::VN; ++u) pf.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, o.v[u], 0, 0);
-  // waves 0-1 (threads < 128) load key scales, waves 2-3 channel scales: the branch is
-  // wave-uniform, so each load sees one scalar descriptor
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (wave < BC / 64) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(ks + k0 * (D / 32), (nkv - k0) * (D / 32));
-    if constexpr (D == 128)
-      pf.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, o.sc, 0, 0);
-    else
-      pf.sc = __builtin_amdgcn_raw_buffer_load_b16(rs, o.sc, 0, 0);
-  } else {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(vs + j * 4, (int64_t)D * kv_pad / 32 - j * 4);
-    pf.sc = __builtin_amdgcn_raw_buffer_load_b32(rs, o.sc, 0, 0);
+  for (int u = 0; u < G::CODE_DMA; ++u) dma16(rv, st + G::OFF_VC + 1024 * (G::CODE_DMA * wave + u), o.v[u]);
+  if (wave < 2) {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(ks + k0 * (D / 32), live ? (nkv - k0) * (D / 32) : 0);
+    // a key's scales are one dword at D = 128, two bytes at D = 64
+    if constexpr (D == 128) dma4(rs, st + G::OFF_KS + 256 * wave, o.s);
+    else dma2(rs, st + G::OFF_KS + 256 * wave, o.s);
+  } else if (lane < D / 2) {
+    const __amdgpu_buffer_rsrc_t rs =
+        rsrc(vs + (int64_t)j * 4, live ? (int64_t)D * kv_pad / 32 - (int64_t)j * 4 : 0);
+    dma4(rs, st + G::OFF_VS + 2 * D * (wave - 2), o.s);
   }
 }
 
-template <int D>
-__device__ __forceinline__ void tile_store(const Prefetch<D>& pf, uint8_t* st, int tid) {
-  constexpr int KCPR = D / 32;
-  uint8_t* kc = st;
-  uint8_t* ksc = st + Lds<D>::KC;
-  uint8_t* vc = ksc + Lds<D>::KS;
-  uint8_t* vsc = vc + Lds<D>::VC;
-#pragma unroll
-  for (int u = 0; u < Prefetch<D>::KN; ++u) {
-    const int ci = tid + NT * u;
-    if (ci < Prefetch<D>::KCHUNKS) {
-      const int kk = ci / KCPR, cc = ci % KCPR;
-      *reinterpret_cast<u32x4*>(kc + kk * (D / 2) + 16 * (cc ^ k_swz<D>(kk))) = pf.k[u];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < Prefetch<D>::VN; ++u) {
-    const int ci = tid + NT * u;
-    if (ci < Prefetch<D>::VCHUNKS) {
-      const int ch = ci / 4, cc = ci % 4;
-      *reinterpret_cast<u32x4*>(vc + ch * 64 + 16 * (cc ^ v_swz(ch))) = pf.v[u];
-    }
-  }
-  if (tid < BC) {
-    const int kk = tid;
-#pragma unroll
-    for (int g = 0; g < D / 32; ++g)
-      ksc[((g * 4 + kk / 32) * 4 + kk % 4) * 8 + (kk % 32) / 4] = (uint8_t)(pf.sc >> (8 * g));
-  } else if (tid < BC + D) {
-    const int ch = tid - BC;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) vsc[(g * 16 + ch % 16) * 8 + ch / 16] = (uint8_t)(pf.sc >> (8 * g));
-  }
+// Gather byte g of each of four dwords (x, y, z, w) into one dword, x in byte 0.
+__device__ __forceinline__ uint32_t gather4(const u32x4& d, uint32_t sel_lo, uint32_t sel_hi) {
+  return __builtin_amdgcn_perm(d.y, d.x, sel_lo) | __builtin_amdgcn_perm(d.w, d.z, sel_hi);
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across, without
+// the memory wait that __syncthreads() adds (the DMA of the next tiles stays in flight).
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
@@ -219,38 +219,36 @@ __device__ __forceinline__ float max32(const v4f (&s)[8]) {
 // live at the same time: S for every group, then softmax + PNQ per group, then
 // the row-sum and P^ V^ products.
 template <int D, int QG, bool PNQ, bool DUMP, bool TAIL>
-__device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int r, int g, int rem,
-                                            const v8i (&qf)[QG], const int (&qsc)[QG],
+__device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int lane, uint32_t sel_lo,
+                                            uint32_t sel_hi, int rem, const v8i (&qf)[QG], const int (&qsc)[QG],
                                             v4f (&acc)[QG][D / 16], v4f (&accl)[QG], float (&m)[QG],
                                             float (&ldir)[QG], float cl, Rule prule, const AttnArgs& a,
                                             const int64_t (&qrow)[QG], int64_t head, int j,
-                                            const uint8_t* lones) {
-  constexpr int NCT = D / 16;
-  const uint8_t* lkc = st;
-  const uint8_t* lks = st + Lds<D>::KC;
-  const uint8_t* lvc = lks + Lds<D>::KS;
-  const uint8_t* lvs = lvc + Lds<D>::VC;
+                                            const uint32_t* lones) {
+  using G = Geo<D>;
+  constexpr int NCT = G::NCT;
+  const int r = lane & 15;  // query within a 16-group / row within an MFMA tile
+  const int g = lane >> 4;  // 32-wide k block of the MFMA operand
   const v4f z = v4f{0, 0, 0, 0};
 
-  // ---- phase 1: S^T = K^ Q^^T.  MFMA t uses keys 32(r/4) + 4t + (r%4) as its 16
-  // rows, so s[qg][t][jj] = S(query, key 32 g + 4 t + jj of this tile).
+  // ---- phase 1: S^T = K^ Q^^T.  MFMA t uses keys kappa(t, r) as its 16 rows, so
+  // s[qg][t][jj] = S(query, key 32 g + 4 t + jj of this tile).
   v4f s[QG][8];
   {
     v8i kf[8];
     int ksw[2];
-    const bool live = g < D / 32;
-    const int key0 = 32 * (r >> 2) + (r & 3);  // the swizzle depends only on key bits 1, 5, 6
-    const uint8_t* kb = lkc + key0 * (D / 2) + 16 * (g ^ k_swz<D>(key0));
+    const bool live = g < G::GK;  // at D = 64 lanes with g >= 2 carry zero operands
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       u32x4 w = u32x4{0u, 0u, 0u, 0u};
-      if (live) w = *reinterpret_cast<const u32x4*>(kb + 4 * t * (D / 2));
+      if (live) w = *reinterpret_cast<const u32x4*>(st + 256 * G::GK * t + 16 * lane);
       kf[t] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
-    uint2 s2 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-    if (live) s2 = *reinterpret_cast<const uint2*>(lks + ((g * 4 + (r >> 2)) * 4 + (r & 3)) * 8);
-    ksw[0] = (int)s2.x;
-    ksw[1] = (int)s2.y;
+    // the scales of keys kappa(0..7, r): byte g of dwords 8r .. 8r + 7
+    const u32x4 s0 = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 32 * r);
+    const u32x4 s1 = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 32 * r + 16);
+    ksw[0] = (int)gather4(s0, sel_lo, sel_hi);
+    ksw[1] = (int)gather4(s1, sel_lo, sel_hi);
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
       s[qg][0] = mma<0>(kf[0], qf[qg], z, ksw[0], qsc[qg]);
@@ -316,15 +314,20 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   v8i vf[NCT];
   int vsw[2];
   {
-    const uint8_t* vb = lvc + r * 64 + 16 * (g ^ v_swz(r));  // v_swz(16 ct + r) = v_swz(r)
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(vb + ct * 16 * 64);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(st + G::OFF_VC + 1024 * ct + 16 * lane);
       vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
-    const uint2 s2 = *reinterpret_cast<const uint2*>(lvs + (g * 16 + r) * 8);
-    vsw[0] = (int)s2.x;
-    vsw[1] = (int)s2.y;
+    // the scales of channels 16 ct + r: byte g of dwords NCT r .. NCT r + NCT - 1
+    const u32x4 s0 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r);
+    vsw[0] = (int)gather4(s0, sel_lo, sel_hi);
+    if constexpr (NCT > 4) {
+      const u32x4 s1 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r + 16);
+      vsw[1] = (int)gather4(s1, sel_lo, sel_hi);
+    } else {
+      vsw[1] = 0;
+    }
   }
   v8i ones;
   {
@@ -356,10 +359,15 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
 // One workgroup = NW waves; wave w owns QG groups of 16 queries.
 template <int D, int QG, bool PNQ, bool DUMP>
 __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
-  constexpr int NCT = D / 16;  // 16-channel tiles of O
+  using G = Geo<D>;
+  constexpr int NCT = G::NCT;       // 16-channel tiles of O
   constexpr int BR = 16 * QG * NW;  // queries per workgroup
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * Lds<D>::STAGE + 16];
-  uint8_t* const lones = lds + 2 * Lds<D>::STAGE;
+  // three tile stages, declared apart so the compiler can tell a DMA into one
+  // stage from reads of another and keeps the DMA in flight across those reads
+  __shared__ __attribute__((aligned(16))) uint8_t st0[G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[G::STAGE];
+  __shared__ __attribute__((aligned(16))) uint32_t lones[4];
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give
   // consecutive work items (same head, neighbouring query tiles) to the same XCD
@@ -373,10 +381,13 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int r = lane & 15;   // query within a 16-group / row within an MFMA tile
-  const int g = lane >> 4;   // 32-wide k block of the MFMA operand
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15;
+  const int g = lane >> 4;
   const int nkv = (int)a.nkv;
+  // v_perm selectors that pick byte g of two dwords (low and high halves of gather4)
+  const uint32_t sel_lo = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0C0C0000u;
+  const uint32_t sel_hi = 0x00000C0Cu | ((uint32_t)g << 16) | ((uint32_t)(g + 4) << 24);
 
   const uint8_t* qc = a.qc + head * a.nq * (D / 2);
   const uint8_t* qs = a.qs + head * a.nq * (D / 32);
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
     const int64_t qq = q < a.nq ? q : a.nq - 1;
     uint4 w = make_uint4(0, 0, 0, 0);
     int sc = 127;
-    if (g < D / 32) {
+    if (g < G::GK) {
       w = *reinterpret_cast<const uint4*>(qc + qq * (D / 2) + 16 * g);
       sc = qs[qq * (D / 32) + g];
     }
@@ -420,38 +431,44 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
   const int ntiles = (nkv + BC - 1) / BC;
   const int nfull = nkv / BC;  // tiles with no padded key
 
-  const LoadOffsets<D> lo = load_offsets<D>(a.kv_pad, tid);
-  Prefetch<D> pf;
-  tile_load<D>(pf, lo, kc, ks, vc, vs, nkv, a.kv_pad, 0, tid);
-  tile_store<D>(pf, lds, tid);
-  if (tid == 0) *reinterpret_cast<uint4*>(lones) = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);
-  __syncthreads();
+  // ---- three-stage ring: tile j lives in stage j % 3; its DMA is issued two tiles
+  // ahead, right after the barrier that retires the reads of the stage it reuses.
+  const DmaOffsets<D> dof = dma_offsets<D>(a.kv_pad, wave, lane);
+  tile_dma<D>(st0, dof, kc, ks, vc, vs, nkv, a.kv_pad, 0, ntiles, wave, lane);
+  tile_dma<D>(st1, dof, kc, ks, vc, vs, nkv, a.kv_pad, 1, ntiles, wave, lane);
+  if (tid < 4) lones[tid] = 0x22222222u;
 
-  // One loop iteration on tile j held in LDS stage S, prefetching tile j+1 into the
-  // other stage.  Full tiles only; the ragged last tile is handled after the loop,
-  // so the loop body carries no masking.
-  auto full_tile = [&](int j, auto stage) {
-    constexpr int S = decltype(stage)::value;
-    const bool more = j + 1 < ntiles;
-    if (more) tile_load<D>(pf, lo, kc, ks, vc, vs, nkv, a.kv_pad, j + 1, tid);
-    attend_tile<D, QG, PNQ, DUMP, false>(lds + S * Lds<D>::STAGE, r, g, BC, qf, qsc, acc, accl, m, ldir, cl,
-                                         prule, a, qrow, head, j, lones);
-    if (more) tile_store<D>(pf, lds + (1 - S) * Lds<D>::STAGE, tid);
-    __syncthreads();
+  // Wait for this wave's DMAs of tile j (those of tile j + 1 may stay in flight);
+  // the barrier then makes every wave's DMAs of tile j visible and guarantees that
+  // every wave is done with tile j - 1, whose stage the DMA of tile j + 2 refills.
+  // Past the last tile the descriptors have size zero: that DMA only writes zeros
+  // into the free stage, and keeps the per-tile DMA count uniform.
+  int sj = 0;  // stage of tile j
+  auto enter = [&](int j) -> const uint8_t* {
+    if constexpr (DUMP) MX_VMCNT(0);  // the P^ dump's stores share the counter
+    else MX_VMCNT(G::NDMA);
+    stage_barrier();
+    uint8_t* cur = sj == 0 ? st0 : (sj == 1 ? st1 : st2);
+    uint8_t* nxt = sj == 0 ? st2 : (sj == 1 ? st0 : st1);
+    tile_dma<D>(nxt, dof, kc, ks, vc, vs, nkv, a.kv_pad, j + 2, ntiles, wave, lane);
+    sj = sj == 2 ? 0 : sj + 1;
+    return cur;
   };
+  // The loop is not unrolled over the three stages: the stage pointers are then
+  // run-time values, and the compiler adds a wait for the DMAs of the previous tile
+  // (issued a whole tile earlier) before the first read, never for the ones just issued.
   int j = 0;
-  for (; j + 1 < nfull; j += 2) {
-    full_tile(j, std::integral_constant<int, 0>{});
-    full_tile(j + 1, std::integral_constant<int, 1>{});
+  for (; j < nfull; ++j) {
+    const uint8_t* cur = enter(j);
+    attend_tile<D, QG, PNQ, DUMP, false>(cur, lane, sel_lo, sel_hi, BC, qf, qsc, acc, accl, m, ldir, cl, prule,
+                                         a, qrow, head, j, lones);
   }
-  if (j < nfull) {
-    full_tile(j, std::integral_constant<int, 0>{});
-    ++j;
+  if (j < ntiles) {  // the ragged last tile, masked
+    const uint8_t* cur = enter(j);
+    attend_tile<D, QG, PNQ, DUMP, true>(cur, lane, sel_lo, sel_hi, nkv - j * BC, qf, qsc, acc, accl, m, ldir, cl,
+                                        prule, a, qrow, head, j, lones);
   }
-  if (j < ntiles) {
-    attend_tile<D, QG, PNQ, DUMP, true>(lds + (j & 1) * Lds<D>::STAGE, r, g, nkv - j * BC, qf, qsc, acc, accl,
-                                        m, ldir, cl, prule, a, qrow, head, j, lones);
-  }
+  MX_VMCNT(0);  // no DMA may still target this workgroup's LDS when it exits
 
   // ---- epilogue: O = O~ / l ; lane holds channels 16ct + 4g + jj of its query
 #pragma unroll
