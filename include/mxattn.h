@@ -123,7 +123,7 @@ size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t 
  *        O~ still uses P^.
  *      O = O~ / l.
  *   Q [B, H, Nq, d]; K, V [B, H, Nkv, d]; O [B, H, Nq, d]; all of dtype `dtype`.
- *   d must be 64 or 128; Nq, Nkv >= 1; softmax_scale finite and > 0.
+ *   d must be 64 or 128; 1 <= Nq, Nkv <= 2^24; softmax_scale finite and > 0.
  *   workspace: device memory of at least mxattn_forward_workspace_bytes(...)
  *   bytes, 256-byte aligned, owned by the caller (contents are scratch).
  * Non-causal, no mask beyond the ragged kv tail.
@@ -140,7 +140,7 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype,
  *   Qc [B, H, Nq, d/2],  Qs [B, H, Nq, d/32]      (AXIS_LAST)
  *   Kc [B, H, Nkv, d/2], Ks [B, H, Nkv, d/32]     (AXIS_LAST)
  *   VTc [B, H, d, P/2],  VTs [B, H, d, P/32]      (AXIS_ROWS, P = mxattn_padded_tokens(Nkv))
- *   O [B, H, Nq, d] in out_dtype.
+ *   O [B, H, Nq, d] in out_dtype.  Shape limits as for mxattn_forward.
  *   p_rule_kind / p_qmax: the scale rule for the P~ tiles.
  *   p_codes, p_scales: either both NULL, or a dump of every quantised P^ tile:
  *   p_codes [B, H, Nq, P/2] and p_scales [B, H, Nq, P/32] (keys past Nkv have

@@ -43,6 +43,9 @@ int64_t round_up(int64_t n, int64_t m) { return (n + m - 1) / m * m; }
 // Largest element count accepted for one tensor (keeps every byte offset and
 // grid size far inside int64 / 31-bit grid limits).
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// Tokens per head (Nq, Nkv) of the attention entry points: keeps every per-head byte
+// count of the kernels below 2^31.
+constexpr int64_t kMaxTokens = int64_t(1) << 24;
 
 bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -61,9 +64,8 @@ int make_rule(int32_t kind, float qmax, mxattn::Rule* r, const char* who) {
   if (kind == MXATTN_RULE_UOS) {
     q = 7.25f;
   } else if (kind == MXATTN_RULE_OCP) {
-    r->ocp = 1;
-    r->q_exp = 0;
-    r->q_frac = 0;
+    r->q_exp = 2;             // e = E - 2 ...
+    r->q_frac = 0xFFFFFFFFu;  // ... whatever the fraction
     return MXATTN_OK;
   } else if (kind == MXATTN_RULE_CEIL) {
     if (!std::isfinite(qmax) || !(qmax > 4.0f) || !(qmax <= 8.0f))
@@ -74,7 +76,6 @@ int make_rule(int32_t kind, float qmax, mxattn::Rule* r, const char* who) {
   }
   uint32_t b;
   std::memcpy(&b, &q, 4);
-  r->ocp = 0;
   r->q_exp = (int)(b >> 23) - 127;
   r->q_frac = b & 0x7FFFFFu;
   return MXATTN_OK;
@@ -118,6 +119,8 @@ int check_attn_shape(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, f
     return fail(MXATTN_E_INVALID, "%s: B, H, Nq, Nkv must be >= 1 (got %lld, %lld, %lld, %lld)", who,
                 (long long)B, (long long)H, (long long)Nq, (long long)Nkv);
   if (d != 64 && d != 128) return fail(MXATTN_E_UNSUPPORTED, "%s: d must be 64 or 128, got %lld", who, (long long)d);
+  if (Nq > kMaxTokens || Nkv > kMaxTokens)
+    return fail(MXATTN_E_INVALID, "%s: Nq and Nkv must be <= %lld tokens per head", who, (long long)kMaxTokens);
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f))
     return fail(MXATTN_E_INVALID, "%s: softmax_scale must be finite and > 0", who);
   int64_t t;

@@ -135,10 +135,20 @@ __device__ __forceinline__ DmaOffsets<D> dma_offsets(int64_t kv_pad, int wave, i
   return o;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, n, 0x00020000);
+// Raw buffer descriptor over `bytes` bytes from `base`; loads at offsets >= bytes
+// return zero without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, 0x00020000);
 }
+
+// One head's tile sources and their sizes in bytes (below 2^31: at most 2^24 tokens).
+struct TileSrc {
+  const uint8_t* kc;
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  int kc_bytes, ks_bytes, vc_bytes, vs_bytes;
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -154,31 +164,29 @@ __device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 2, off, 0, 0, 0);
 }
 
-// Issue the DMAs of tile j into stage `st`: NDMA instructions per wave.  Buffer
+// Issue the DMAs of tile j into stage `st`: NDMA instructions per wave.  The buffer
 // descriptors are rebuilt per tile on the scalar unit (base at the tile, size = bytes
 // left), so keys past the last one, and whole tiles past the end, read as zero
-// without touching memory.
+// without touching memory.  Past the end the V^ descriptors still cover the head's
+// other channels: those reads stay inside the head's V^ and are never used.
 template <int D>
-__device__ __forceinline__ void tile_dma(uint8_t* st, const DmaOffsets<D>& o, const uint8_t* kc,
-                                         const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int nkv,
-                                         int64_t kv_pad, int j, int ntiles, int wave, int lane) {
+__device__ __forceinline__ void tile_dma(uint8_t* st, const DmaOffsets<D>& o, const TileSrc& src, int j, int wave,
+                                         int lane) {
   using G = Geo<D>;
-  const bool live = j < ntiles;
-  const int64_t k0 = (int64_t)j * BC;
-  const __amdgpu_buffer_rsrc_t rk = rsrc(kc + k0 * (D / 2), live ? (nkv - k0) * (D / 2) : 0);
-  const __amdgpu_buffer_rsrc_t rv = rsrc(vc + (int64_t)j * 64, live ? (int64_t)D * kv_pad / 2 - (int64_t)j * 64 : 0);
+  const int kc0 = j * (BC * D / 2), ks0 = j * (BC * D / 32);
+  const __amdgpu_buffer_rsrc_t rk = rsrc(src.kc + kc0, max(src.kc_bytes - kc0, 0));
+  const __amdgpu_buffer_rsrc_t rv = rsrc(src.vc + 64 * j, src.vc_bytes - 64 * j);
 #pragma unroll
   for (int u = 0; u < G::CODE_DMA; ++u) dma16(rk, st + 1024 * (G::CODE_DMA * wave + u), o.k[u]);
 #pragma unroll
   for (int u = 0; u < G::CODE_DMA; ++u) dma16(rv, st + G::OFF_VC + 1024 * (G::CODE_DMA * wave + u), o.v[u]);
   if (wave < 2) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(ks + k0 * (D / 32), live ? (nkv - k0) * (D / 32) : 0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(src.ks + ks0, max(src.ks_bytes - ks0, 0));
     // a key's scales are one dword at D = 128, two bytes at D = 64
     if constexpr (D == 128) dma4(rs, st + G::OFF_KS + 256 * wave, o.s);
     else dma2(rs, st + G::OFF_KS + 256 * wave, o.s);
   } else if (lane < D / 2) {
-    const __amdgpu_buffer_rsrc_t rs =
-        rsrc(vs + (int64_t)j * 4, live ? (int64_t)D * kv_pad / 32 - (int64_t)j * 4 : 0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(src.vs + 4 * j, src.vs_bytes - 4 * j);
     dma4(rs, st + G::OFF_VS + 2 * D * (wave - 2), o.s);
   }
 }
@@ -214,10 +222,97 @@ __device__ __forceinline__ float max32(const v4f (&s)[8]) {
   return fmaxf(fmax3(w0, w1, w2), w3);
 }
 
-// One kv tile for one wave's QG query groups.  `rem` (TAIL only) is the number of
-// valid keys in the tile.  Three phases keep the K^ and V^ fragments from being
-// live at the same time: S for every group, then softmax + PNQ per group, then
-// the row-sum and P^ V^ products.
+// S^T MFMAs of one 16-query group: s[t][jj] = S(query, key 32 g + 4 t + jj of the tile).
+__device__ __forceinline__ void s_mfma(v4f (&s)[8], const v8i (&kf)[8], const int (&ksw)[2], const v8i& qf,
+                                       int qsc) {
+  const v4f z = v4f{0, 0, 0, 0};
+  s[0] = mma<0>(kf[0], qf, z, ksw[0], qsc);
+  s[1] = mma<1>(kf[1], qf, z, ksw[0], qsc);
+  s[2] = mma<2>(kf[2], qf, z, ksw[0], qsc);
+  s[3] = mma<3>(kf[3], qf, z, ksw[0], qsc);
+  s[4] = mma<0>(kf[4], qf, z, ksw[1], qsc);
+  s[5] = mma<1>(kf[5], qf, z, ksw[1], qsc);
+  s[6] = mma<2>(kf[6], qf, z, ksw[1], qsc);
+  s[7] = mma<3>(kf[7], qf, z, ksw[1], qsc);
+}
+
+// Softmax, plain-ALU part: masks keys past the end (TAIL), updates the running max m
+// from the block max and the row max over the 4 lanes of the query, and turns s into
+// the exponent arguments x = (S - m') * softmax_scale * log2(e).  Returns the block
+// max's argument (bm - m') * cl; alpha = exp2((m - m') cl) is the running-state factor.
+template <bool TAIL>
+__device__ __forceinline__ float soft_alu(v4f (&s)[8], float& m, float cl, int lim, float& alpha) {
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (4 * t + jj >= lim) s[t][jj] = -INFINITY;
+  }
+  const float bm = max32(s);
+  const float mnew = fmaxf(m, xmax4(bm));
+  alpha = __builtin_amdgcn_exp2f((m - mnew) * cl);
+  m = mnew;
+  const float mc = mnew * cl;
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) s[t][jj] = __builtin_fmaf(s[t][jj], cl, -mc);
+  return (bm - mnew) * cl;
+}
+
+// Softmax, transcendental part: P~ = exp2(x) and its PNQ quantisation, once, in the
+// lane's aligned 32-key block.  The block max of P~ is exp2 of the block max's
+// argument (exactly 1 where the block holds the row max).
+__device__ __forceinline__ void soft_exp(const v4f (&x)[8], float xm, Rule prule, float (&p)[32], uint32_t (&pc)[4],
+                                         int& psc) {
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) p[4 * t + jj] = __builtin_amdgcn_exp2f(x[t][jj]);
+  const float pm = __builtin_amdgcn_exp2f(xm);
+  const int e = mx_exponent(__float_as_uint(pm), prule);
+  quant32(p, e, pc);
+  psc = e + 127;
+}
+
+// O~^T += V^^T P^^T for one group, plus the PNQ row sum as a ones MFMA over the same P^.
+template <int D, bool PNQ>
+__device__ __forceinline__ void pv_mfma(v4f (&acc)[D / 16], v4f& accl, const v8i (&vf)[D / 16], const int (&vsw)[2],
+                                        const v8i& ones, const v8i& pf8, int psc) {
+  constexpr int NCT = D / 16;
+  if constexpr (PNQ) accl = mma<0>(ones, pf8, accl, 127, psc);
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if ((ct & 3) == 0) acc[ct] = mma<0>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
+    if ((ct & 3) == 1) acc[ct] = mma<1>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
+    if ((ct & 3) == 2) acc[ct] = mma<2>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
+    if ((ct & 3) == 3) acc[ct] = mma<3>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
+  }
+}
+
+// Make the compiler produce the eight accumulator tiles at this point of the program
+// (it would otherwise sink work past the branches that follow).
+__device__ __forceinline__ void pin(v4f (&x)[8]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+}
+
+// Interleave the next N MFMAs of the scheduling region with K ALU/transcendental
+// instructions each, so the exponentials and conversions of one group execute in
+// the shadow of the other group's matrix products.
+template <int N, int K>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002 | 0x400, K, 0);  // K VALU / TRANS
+  }
+}
+
+// One kv tile for one wave's two 16-query groups (q0, q1).  The order overlaps
+// each group's transcendental softmax work with the other group's MFMAs:
+//   S(q0) | ALU(q0) | S(q1) + EXP(q0) | ALU(q1) | rescale | PV(q0) + EXP(q1) | PV(q1)
+// `rem` (TAIL only) is the number of valid keys in the tile.
 template <int D, int QG, bool PNQ, bool DUMP, bool TAIL>
 __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int lane, uint32_t sel_lo,
                                             uint32_t sel_hi, int rem, const v8i (&qf)[QG], const int (&qsc)[QG],
@@ -225,18 +320,17 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
                                             float (&ldir)[QG], float cl, Rule prule, const AttnArgs& a,
                                             const int64_t (&qrow)[QG], int64_t head, int j,
                                             const uint32_t* lones) {
+  static_assert(QG == 2, "the tile schedule pairs two query groups");
   using G = Geo<D>;
   constexpr int NCT = G::NCT;
   const int r = lane & 15;  // query within a 16-group / row within an MFMA tile
   const int g = lane >> 4;  // 32-wide k block of the MFMA operand
-  const v4f z = v4f{0, 0, 0, 0};
+  const int lim = rem - 32 * g;  // keys of this lane's block that exist (TAIL)
 
-  // ---- phase 1: S^T = K^ Q^^T.  MFMA t uses keys kappa(t, r) as its 16 rows, so
-  // s[qg][t][jj] = S(query, key 32 g + 4 t + jj of this tile).
-  v4f s[QG][8];
+  // K^ fragments: MFMA t uses keys kappa(t, r) as its 16 rows
+  v8i kf[8];
+  int ksw[2];
   {
-    v8i kf[8];
-    int ksw[2];
     const bool live = g < G::GK;  // at D = 64 lanes with g >= 2 carry zero operands
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -249,68 +343,34 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     const u32x4 s1 = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 32 * r + 16);
     ksw[0] = (int)gather4(s0, sel_lo, sel_hi);
     ksw[1] = (int)gather4(s1, sel_lo, sel_hi);
-#pragma unroll
-    for (int qg = 0; qg < QG; ++qg) {
-      s[qg][0] = mma<0>(kf[0], qf[qg], z, ksw[0], qsc[qg]);
-      s[qg][1] = mma<1>(kf[1], qf[qg], z, ksw[0], qsc[qg]);
-      s[qg][2] = mma<2>(kf[2], qf[qg], z, ksw[0], qsc[qg]);
-      s[qg][3] = mma<3>(kf[3], qf[qg], z, ksw[0], qsc[qg]);
-      s[qg][4] = mma<0>(kf[4], qf[qg], z, ksw[1], qsc[qg]);
-      s[qg][5] = mma<1>(kf[5], qf[qg], z, ksw[1], qsc[qg]);
-      s[qg][6] = mma<2>(kf[6], qf[qg], z, ksw[1], qsc[qg]);
-      s[qg][7] = mma<3>(kf[7], qf[qg], z, ksw[1], qsc[qg]);
-    }
   }
 
-  // ---- phase 2: online softmax and PNQ quantisation of P~, per query group
-  v8i pf8[QG];
-  int psc[QG];
-  float alpha[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    if constexpr (TAIL) {
-      const int lim = rem - 32 * g;  // keys of this lane's block that exist
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (4 * t + jj >= lim) s[qg][t][jj] = -INFINITY;
-    }
-    // block max, row max (4 lanes), running max
-    const float bm = max32(s[qg]);
-    const float mnew = fmaxf(m[qg], xmax4(bm));
-    alpha[qg] = __builtin_amdgcn_exp2f((m[qg] - mnew) * cl);
-    m[qg] = mnew;
-    const float mc = mnew * cl;
-    // P~ = exp(S - m'); its block max is exp(bm - m'), exactly 1 where bm = m'
-    float p[32];
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        p[4 * t + jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][t][jj], cl, -mc));
-    const float pm = __builtin_amdgcn_exp2f((bm - mnew) * cl);
-    // PNQ: quantise P~ once, in this lane's aligned 32-key block
-    const int e = mx_exponent(__float_as_uint(pm), prule);
-    uint32_t pc[4];
-    quant32(p, e, pc);
-    pf8[qg] = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
-    psc[qg] = e + 127;
-    if constexpr (!PNQ) {
-      float ls = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) ls += p[k];
-      ldir[qg] = ldir[qg] * alpha[qg] + xsum4(ls);
-    }
-    if (DUMP && qrow[qg] < a.nq) {
-      const int64_t prow = head * a.nq + qrow[qg];
-      const int64_t key0 = (int64_t)j * BC + 32 * g;
-      *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) = make_uint4(pc[0], pc[1], pc[2], pc[3]);
-      a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)psc[qg];
-    }
-  }
+  v4f s0[8], s1[8];
+  float alpha0, alpha1, p[32];
+  int psc0, psc1;
+  uint32_t pc0[4], pc1[4];
 
-  // ---- phase 3: rescale, row sum and O~^T += V^^T P^^T
+  s_mfma(s0, kf, ksw, qf[0], qsc[0]);
+  const float xm0 = soft_alu<TAIL>(s0, m[0], cl, lim, alpha0);
+  pin(s0);
+  __builtin_amdgcn_sched_barrier(0);
+  s_mfma(s1, kf, ksw, qf[1], qsc[1]);
+  soft_exp(s0, xm0, prule, p, pc0, psc0);
+  if constexpr (!PNQ) {
+    float ls = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) ls += p[k];
+    ldir[0] = ldir[0] * alpha0 + xsum4(ls);
+  }
+  interleave_mfma<8, 6>();
+  // keep group 0's quantisation here: its only consumers come after the rescale
+  // branches below, past which the compiler would otherwise sink it
+  asm volatile("" : "+v"(pc0[0]), "+v"(pc0[1]), "+v"(pc0[2]), "+v"(pc0[3]), "+v"(psc0));
+  __builtin_amdgcn_sched_barrier(0);
+  const float xm1 = soft_alu<TAIL>(s1, m[1], cl, lim, alpha1);
+  pin(s1);
+
+  // V^ fragments (A operand of O^T): channels 16 ct + r, keys 32 g .. 32 g + 31
   v8i vf[NCT];
   int vsw[2];
   {
@@ -320,11 +380,11 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
       vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
     // the scales of channels 16 ct + r: byte g of dwords NCT r .. NCT r + NCT - 1
-    const u32x4 s0 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r);
-    vsw[0] = (int)gather4(s0, sel_lo, sel_hi);
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r);
+    vsw[0] = (int)gather4(v0, sel_lo, sel_hi);
     if constexpr (NCT > 4) {
-      const u32x4 s1 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r + 16);
-      vsw[1] = (int)gather4(s1, sel_lo, sel_hi);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r + 16);
+      vsw[1] = (int)gather4(v1, sel_lo, sel_hi);
     } else {
       vsw[1] = 0;
     }
@@ -336,22 +396,44 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     const u32x4 w = *reinterpret_cast<const u32x4*>(lones);
     ones = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
   }
+  // rescale the running state of a group when any of its rows' max moved (alpha == 1 is exact)
+  if (__builtin_amdgcn_ballot_w64(alpha0 != 1.0f)) {
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    // rescale the running state when any row's max moved (alpha == 1 is exact)
-    if (__builtin_amdgcn_ballot_w64(alpha[qg] != 1.0f)) {
+    for (int ct = 0; ct < NCT; ++ct) acc[0][ct] *= alpha0;
+    accl[0] *= alpha0;
+  }
+  if (__builtin_amdgcn_ballot_w64(alpha1 != 1.0f)) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] *= alpha[qg];
-      accl[qg] *= alpha[qg];
-    }
-    // row sum: PNQ sums the same P^ with a ones MFMA (direct placement summed P~ above)
-    if constexpr (PNQ) accl[qg] = mma<0>(ones, pf8[qg], accl[qg], 127, psc[qg]);
+    for (int ct = 0; ct < NCT; ++ct) acc[1][ct] *= alpha1;
+    accl[1] *= alpha1;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  pv_mfma<D, PNQ>(acc[0], accl[0], vf, vsw, ones, v8i{(int)pc0[0], (int)pc0[1], (int)pc0[2], (int)pc0[3], 0, 0, 0, 0},
+                  psc0);
+  soft_exp(s1, xm1, prule, p, pc1, psc1);
+  if constexpr (!PNQ) {
+    float ls = 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      if ((ct & 3) == 0) acc[qg][ct] = mma<0>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
-      if ((ct & 3) == 1) acc[qg][ct] = mma<1>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
-      if ((ct & 3) == 2) acc[qg][ct] = mma<2>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
-      if ((ct & 3) == 3) acc[qg][ct] = mma<3>(vf[ct], pf8[qg], acc[qg][ct], vsw[ct >> 2], psc[qg]);
+    for (int k = 0; k < 32; ++k) ls += p[k];
+    ldir[1] = ldir[1] * alpha1 + xsum4(ls);
+  }
+  interleave_mfma<NCT + 1, 6>();
+  __builtin_amdgcn_sched_barrier(0);
+  pv_mfma<D, PNQ>(acc[1], accl[1], vf, vsw, ones, v8i{(int)pc1[0], (int)pc1[1], (int)pc1[2], (int)pc1[3], 0, 0, 0, 0},
+                  psc1);
+
+  if constexpr (DUMP) {
+    const uint32_t* pcs[2] = {pc0, pc1};
+    const int pscs[2] = {psc0, psc1};
+#pragma unroll
+    for (int qg = 0; qg < 2; ++qg) {
+      if (qrow[qg] < a.nq) {
+        const int64_t prow = head * a.nq + qrow[qg];
+        const int64_t key0 = (int64_t)j * BC + 32 * g;
+        *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) =
+            make_uint4(pcs[qg][0], pcs[qg][1], pcs[qg][2], pcs[qg][3]);
+        a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)pscs[qg];
+      }
     }
   }
 }
@@ -391,10 +473,10 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
 
   const uint8_t* qc = a.qc + head * a.nq * (D / 2);
   const uint8_t* qs = a.qs + head * a.nq * (D / 32);
-  const uint8_t* kc = a.kc + head * a.nkv * (D / 2);
-  const uint8_t* ks = a.ks + head * a.nkv * (D / 32);
-  const uint8_t* vc = a.vc + head * (int64_t)D * (a.kv_pad / 2);
-  const uint8_t* vs = a.vs + head * (int64_t)D * (a.kv_pad / 32);
+  const int kvp = (int)a.kv_pad;
+  const TileSrc src{a.kc + head * a.nkv * (D / 2), a.ks + head * a.nkv * (D / 32),
+                    a.vc + head * (int64_t)D * (kvp / 2), a.vs + head * (int64_t)D * (kvp / 32),
+                    nkv * (D / 2), nkv * (D / 32), D * (kvp / 2), D * (kvp / 32)};
 
   // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop
   v8i qf[QG];
@@ -434,8 +516,8 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
   // ---- three-stage ring: tile j lives in stage j % 3; its DMA is issued two tiles
   // ahead, right after the barrier that retires the reads of the stage it reuses.
   const DmaOffsets<D> dof = dma_offsets<D>(a.kv_pad, wave, lane);
-  tile_dma<D>(st0, dof, kc, ks, vc, vs, nkv, a.kv_pad, 0, ntiles, wave, lane);
-  tile_dma<D>(st1, dof, kc, ks, vc, vs, nkv, a.kv_pad, 1, ntiles, wave, lane);
+  tile_dma<D>(st0, dof, src, 0, wave, lane);
+  tile_dma<D>(st1, dof, src, 1, wave, lane);
   if (tid < 4) lones[tid] = 0x22222222u;
 
   // Wait for this wave's DMAs of tile j (those of tile j + 1 may stay in flight);
@@ -450,7 +532,7 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
     stage_barrier();
     uint8_t* cur = sj == 0 ? st0 : (sj == 1 ? st1 : st2);
     uint8_t* nxt = sj == 0 ? st2 : (sj == 1 ? st0 : st1);
-    tile_dma<D>(nxt, dof, kc, ks, vc, vs, nkv, a.kv_pad, j + 2, ntiles, wave, lane);
+    tile_dma<D>(nxt, dof, src, j + 2, wave, lane);
     sj = sj == 2 ? 0 : sj + 1;
     return cur;
   };

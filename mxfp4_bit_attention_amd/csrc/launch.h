@@ -6,10 +6,12 @@
 
 namespace mxattn {
 
-// Shared-scale rule in the form the kernels use.  CEIL(q) with q = 1.g * 2^q_exp
-// (UOS is CEIL(7.25)); ocp = 1 selects the floor rule e = floor(log2 M) - 2.
+// Shared-scale rule in the form the kernels use: for a block max M = 1.f * 2^E the
+// shared exponent is e = E - q_exp + (f > q_frac), f and q_frac being 23-bit
+// fractions.  CEIL(q) with q = 1.g * 2^q_exp (UOS is CEIL(7.25)) sets q_frac = g;
+// the OCP floor rule e = floor(log2 M) - 2 sets q_exp = 2 and a q_frac no fraction
+// exceeds, so one branch-free formula serves every rule.
 struct Rule {
-  int ocp;
   int q_exp;
   uint32_t q_frac;
 };

@@ -18,14 +18,14 @@ namespace mxattn {
 // (finite, non-negative; zero and subnormals allowed).
 //  CEIL(q): the smallest e with M <= q 2^e.  With M = 1.f 2^E and q = 1.g 2^qe,
 //           that is E - qe when f <= g and E - qe + 1 otherwise.
-//  OCP:     E - 2.
+//  OCP:     E - 2 (encoded as qe = 2 with a g that no f exceeds).
 // The result is clamped to [-127, 127].  Every M below 2^-126 (zero and
 // subnormals included) needs e <= -127 under any rule with q >= 4, so reading E
 // from the biased exponent field (E = -127 for those) and clamping is exact.
 __device__ __forceinline__ int mx_exponent(uint32_t mbits, Rule r) {
   const int E = (int)(mbits >> 23) - 127;
   const uint32_t f = mbits & 0x7FFFFFu;
-  const int e = r.ocp ? (E - 2) : (E - r.q_exp + (f > r.q_frac ? 1 : 0));
+  const int e = E - r.q_exp + (f > r.q_frac ? 1 : 0);
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 

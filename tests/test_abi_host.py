@@ -107,6 +107,8 @@ def f_call(mx, Q=FAKE, dtype=1, B=1, H=2, Nq=256, Nkv=256, d=128, scale=0.125, h
     (dict(ws_bytes=100), -3, "workspace"),
     (dict(kind=2, qmax=9.0), -1, "(4, 8]"),
     (dict(H=70000), -1, "65535"),
+    (dict(Nkv=(1 << 24) + 1), -1, "tokens per head"),
+    (dict(Nq=(1 << 24) + 1), -1, "tokens per head"),
 ])
 def test_forward_rejects_bad_arguments(mx, kw, status, msg):
     assert f_call(mx, **kw) == status
