@@ -82,7 +82,8 @@ int64_t mxattn_padded_tokens(int64_t n);
  *   axis    MXATTN_AXIS_LAST: cols must be a multiple of 32; with hadamard != 0
  *             cols must be 64 or 128.
  *             codes  [batch, rows, cols/2]   scales [batch, rows, cols/32]
- *           MXATTN_AXIS_ROWS: cols must be even; hadamard must be 0.  With
+ *           MXATTN_AXIS_ROWS: cols must be even and <= 65536, batch <= 65535;
+ *             hadamard must be 0.  With
  *             P = mxattn_padded_tokens(rows):
  *             codes  [batch, cols, P/2]      scales [batch, cols, P/32]
  *             (each column's blocks run along rows; rows past `rows` are zeros,

@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libmxattn.so`` behind the C ABI declared in ``include/mxattn.h``.
 PyTorch supplies device memory and the current stream.  The library must be
-built first (``python -m mxfp4_bit_attention_amd.build``); importing this
+built first (``python mxfp4_bit_attention_amd/build.py``); importing this
 module raises if it is missing, and nothing here falls back to a CPU path.
 
 Names mirror the C entry points: ``mxattn_quantize``, ``mxattn_forward``,
@@ -42,7 +42,7 @@ class MxattnError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m mxfp4_bit_attention_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python mxfp4_bit_attention_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     c = ctypes
     vp, i32, i64, u32, f32, sz = c.c_void_p, c.c_int32, c.c_int64, c.c_uint32, c.c_float, c.c_size_t

@@ -1,6 +1,9 @@
 """Build libmxattn.so (HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m mxfp4_bit_attention_amd.build
+    python mxfp4_bit_attention_amd/build.py
+
+(run as a script: importing the package itself loads the library, which may not
+exist yet or may be stale).
 
 Every HIP translation unit is compiled with IEEE-exact fp32 settings (no
 contraction into FMA, denormals kept) because the quantiser must reproduce

@@ -173,8 +173,8 @@ int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, i
   } else if (axis == MXATTN_AXIS_ROWS) {
     if (hadamard) return fail(MXATTN_E_INVALID, "%s: AXIS_ROWS does not take a Hadamard rotation", who);
     if (cols % 2) return fail(MXATTN_E_INVALID, "%s: cols must be even for AXIS_ROWS", who);
-    if (batch > 65535 || (cols + 127) / 128 > 65535)
-      return fail(MXATTN_E_INVALID, "%s: batch and cols/128 must be <= 65535 for AXIS_ROWS", who);
+    if (batch > 65535 || cols > 65536)
+      return fail(MXATTN_E_INVALID, "%s: AXIS_ROWS needs batch <= 65535 and cols <= 65536", who);
     const int64_t P = round_up(rows, mxattn::kKvTile);
     e = mxattn::launch_quant_rows(x, eb, batch, rows, cols, P, codes, scales, rule, s);
   } else {

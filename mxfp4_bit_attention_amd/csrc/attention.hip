@@ -150,20 +150,6 @@ struct TileSrc {
   int kc_bytes, ks_bytes, vc_bytes, vs_bytes;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Global->LDS DMA of 16, 4 or 2 bytes per lane: lane L writes at lds + 16 L (the 4- and
-// 2-byte forms at lds + 4 L, zero-extended); `lds` must be the same in every lane.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
-}
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
-}
-__device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 2, off, 0, 0, 0);
-}
-
 // Issue the DMAs of tile j into stage `st`: NDMA instructions per wave.  The buffer
 // descriptors are rebuilt per tile on the scalar unit (base at the tile, size = bytes
 // left), so keys past the last one, and whole tiles past the end, read as zero

@@ -58,6 +58,41 @@ __device__ __forceinline__ void quant32(const float* v, int e, uint32_t out[4]) 
   }
 }
 
+// Largest |v[i]| of a 32-element block as fp32 bits, with the NaN-propagating
+// maximum (v_maximum3_f32 with |.| operand modifiers): the result, sign cleared,
+// is >= 0x7F800000 exactly when some element is not finite, and is otherwise the
+// bit pattern of the largest magnitude.
+__device__ __forceinline__ float amax2(float a, float b) {
+  return __builtin_elementwise_maximum(__builtin_fabsf(a), __builtin_fabsf(b));
+}
+__device__ __forceinline__ float amax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(amax2(a, b), __builtin_fabsf(c));
+}
+__device__ __forceinline__ uint32_t absmax32_bits(const float* v) {
+  float u[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) u[i] = amax3(v[3 * i], v[3 * i + 1], v[3 * i + 2]);
+  u[10] = amax2(v[30], v[31]);
+  const float w0 = amax3(u[0], u[1], u[2]), w1 = amax3(u[3], u[4], u[5]);
+  const float w2 = amax3(u[6], u[7], u[8]), w3 = amax2(u[9], u[10]);
+  return __float_as_uint(amax2(amax3(w0, w1, w2), w3)) & 0x7FFFFFFFu;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Global->LDS DMA of 16, 4 or 2 bytes per lane through a raw buffer descriptor:
+// lane L writes at lds + 16 L (the 4- and 2-byte forms at lds + 4 L, zero-extended);
+// `lds` must be the same in every lane, and offsets past the descriptor's size read 0.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 2, off, 0, 0, 0);
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

@@ -21,124 +21,159 @@
 
 namespace mxattn {
 
-// Non-finite marker and the block max of |x| taken on the fp32 bit patterns:
-// for non-negative floats integer order is float order, and NaN/Inf patterns
-// sort above every finite value, so max >= 0x7F800000 flags a non-finite block.
-__device__ __forceinline__ uint32_t absbits(float x) { return __float_as_uint(x) & 0x7FFFFFFFu; }
 
 // ---------------------------------------------------------------------------
 // Fused Hadamard + quantise.  D in {64, 128}; EB = bytes per input element (2 = bf16, 4 = fp32).
-// One row is held by LPR = D/64 lanes, 64 elements each; a 256-thread block
-// handles ROWS = 256/LPR rows.  The tile is read from HBM with fully coalesced
-// 16-byte loads into LDS (rows padded by 16 bytes so that the per-lane row reads
-// are bank-conflict free), then each lane reads its 64 elements.
+// One row is held by LPR = D/64 lanes, 64 elements each, so a wave handles a chunk
+// of RW = 64/LPR rows at a time.  Waves work independently and persistently: wave w
+// of W takes chunks w, w + W, w + 2W, ...  Each chunk is brought into the wave's own
+// LDS buffer by global->LDS DMA; as soon as the lanes have read it into registers the
+// DMA of the wave's next chunk is issued, so it lands while this chunk is rotated,
+// quantised and stored.  In LDS, 16-byte unit q of row r sits at q ^ swz(r), which
+// makes the per-lane row reads bank-conflict free.
 // Butterflies h = 1..32 run inside the lane; for D = 128 the h = 64 stage pairs
 // the two lanes of a row through a DPP quad permute (lanes 2r, 2r+1).
+template <int D, int EB>
+struct HadGeo {
+  static constexpr int LPR = D / 64;          // lanes per row
+  static constexpr int RW = 64 / LPR;         // rows per wave chunk
+  static constexpr int RB = D * EB;           // bytes per row
+  static constexpr int CH = RB / 16;          // 16-byte units per row
+  static constexpr int CB = RW * RB;          // bytes per chunk (8 or 16 KB)
+  static constexpr int NDMA = CB / 1024;      // 1 KB DMAs per chunk
+  static constexpr int NW = 4;                // waves per workgroup
+  // swizzle of row r: the 16 (or 8) lanes of one LDS read cycle hit distinct units
+  __device__ static int swz(int r) {
+    if constexpr (D == 128 && EB == 2) return r & 7;         // 16 units/row, lanes read 8 each
+    else if constexpr (D == 64 && EB == 2) return (r >> 1) & 7;  // 8 units/row, 2 rows per 256 B
+    else return r & 15;                                        // fp32: 32 or 16 units/row
+  }
+};
+
 template <int D, int EB>
 __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restrict__ x, int64_t nrows,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales, Rule rule,
-                                                        float c) {
-  constexpr int LPR = D / 64;
-  constexpr int ROWS = 256 / LPR;
-  constexpr int ROW_BYTES = D * EB;
-  constexpr int STRIDE = ROW_BYTES + 16;
-  constexpr int CH_PER_ROW = ROW_BYTES / 16;
-  constexpr int NCH = ROWS * CH_PER_ROW;  // 16-byte chunks in the tile
-  __shared__ __attribute__((aligned(16))) uint8_t tile[ROWS * STRIDE];
+                                                        float c, int64_t nchunks) {
+  using G = HadGeo<D, EB>;
+  constexpr int LPR = G::LPR;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::NW * G::CB];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* buf = lds + wave * G::CB;
+  const int64_t W = (int64_t)gridDim.x * G::NW;
+  int64_t chunk = (int64_t)blockIdx.x * G::NW + wave;
+  const int64_t total = nrows * G::RB;
 
-  const int tid = threadIdx.x;
-  const int64_t row0 = (int64_t)blockIdx.x * ROWS;
-  const int64_t left = nrows - row0;
-  const int nr = left < ROWS ? (int)left : ROWS;
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + row0 * ROW_BYTES);
-  const int nch_valid = nr * CH_PER_ROW;
+  // per-lane DMA source offsets within a chunk (the same for every chunk)
+  uint32_t doff[G::NDMA];
 #pragma unroll
-  for (int k = 0; k < NCH / 256; ++k) {
-    const int ch = tid + 256 * k;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (ch < nch_valid) {
-      const u32x4 w = __builtin_nontemporal_load(src + ch);  // streamed once: do not keep in cache
-      v = make_uint4(w.x, w.y, w.z, w.w);
-    }
-    const int r = ch / CH_PER_ROW, q = ch % CH_PER_ROW;
-    *reinterpret_cast<uint4*>(tile + r * STRIDE + 16 * q) = v;
+  for (int u = 0; u < G::NDMA; ++u) {
+    const int slot = 64 * u + lane;  // 16-byte unit of the LDS chunk
+    const int r = slot / G::CH, pos = slot % G::CH;
+    doff[u] = (uint32_t)(r * G::RB + 16 * (pos ^ G::swz(r)));
   }
-  __syncthreads();
+  auto issue = [&](int64_t ch) {
+    const int64_t left = total - ch * G::CB;
+    const int n = left <= 0 ? 0 : (left > 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(x + (ch < nchunks ? ch : 0) * G::CB), (short)0, n,
+                                          0x00020000);
+#pragma unroll
+    for (int u = 0; u < G::NDMA; ++u)
+      dma16(rs, buf + 1024 * u, doff[u]);
+  };
 
-  const int lr = tid / LPR;     // row within the tile
-  const int half = tid % LPR;   // which 64 elements of the row
-  float v[64];
-  {
-    const uint8_t* p = tile + lr * STRIDE + half * 64 * EB;
-    if constexpr (EB == 2) {
+  const int lr = lane / LPR;    // row within the chunk
+  const int half = lane % LPR;  // which 64 elements of the row
+  // The stores of a chunk are issued one iteration late, after the next chunk has
+  // been read from LDS: the wait the compiler places before those reads (for the DMA
+  // that filled the buffer) then never waits on stores issued just before it.
+  uint32_t q[2][4];
+  uint32_t sb2 = 0;
+  int64_t prow = -1;  // row whose results q / sb2 hold (-1: none)
+  auto store = [&]() {
+    if (prow >= 0 && prow < nrows) {
+      uint8_t* crow = codes + prow * (D / 2) + half * 32;
+      *reinterpret_cast<uint4*>(crow) = make_uint4(q[0][0], q[0][1], q[0][2], q[0][3]);
+      *reinterpret_cast<uint4*>(crow + 16) = make_uint4(q[1][0], q[1][1], q[1][2], q[1][3]);
+      *reinterpret_cast<uint16_t*>(scales + prow * (D / 32) + half * 2) = (uint16_t)sb2;
+    }
+  };
+  if (chunk < nchunks) issue(chunk);
+  for (; chunk < nchunks; chunk += W) {
+    float v[64];
+    {
+      const uint8_t* p = buf + lr * G::RB;
+      if constexpr (EB == 2) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint4 w = *reinterpret_cast<const uint4*>(p + 16 * q);
-        v[8 * q + 0] = bf16lo(w.x); v[8 * q + 1] = bf16hi(w.x);
-        v[8 * q + 2] = bf16lo(w.y); v[8 * q + 3] = bf16hi(w.y);
-        v[8 * q + 4] = bf16lo(w.z); v[8 * q + 5] = bf16hi(w.z);
-        v[8 * q + 6] = bf16lo(w.w); v[8 * q + 7] = bf16hi(w.w);
-      }
-    } else {
+        for (int k = 0; k < 8; ++k) {
+          const uint4 w = *reinterpret_cast<const uint4*>(p + 16 * ((8 * half + k) ^ G::swz(lr)));
+          v[8 * k + 0] = bf16lo(w.x); v[8 * k + 1] = bf16hi(w.x);
+          v[8 * k + 2] = bf16lo(w.y); v[8 * k + 3] = bf16hi(w.y);
+          v[8 * k + 4] = bf16lo(w.z); v[8 * k + 5] = bf16hi(w.z);
+          v[8 * k + 6] = bf16lo(w.w); v[8 * k + 7] = bf16hi(w.w);
+        }
+      } else {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        float4 w = *reinterpret_cast<const float4*>(p + 16 * q);
-        v[4 * q + 0] = w.x; v[4 * q + 1] = w.y; v[4 * q + 2] = w.z; v[4 * q + 3] = w.w;
+        for (int k = 0; k < 16; ++k) {
+          const float4 w = *reinterpret_cast<const float4*>(p + 16 * ((16 * half + k) ^ G::swz(lr)));
+          v[4 * k + 0] = w.x; v[4 * k + 1] = w.y; v[4 * k + 2] = w.z; v[4 * k + 3] = w.w;
+        }
       }
     }
-  }
-  // in-lane butterflies h = 1, 2, 4, 8, 16, 32 (element index bits 0..5)
-#pragma unroll
-  for (int h = 1; h < 64; h *= 2) {
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-    }
-  }
-  if constexpr (LPR == 2) {
-    // h = 64: lane 2r holds elements 0..63 (the "a" side), lane 2r+1 holds 64..127.
-    // a-lane: own + partner = a + b;  b-lane: partner + (-own) = a - b.
-    const uint32_t sgn = (uint32_t)half << 31;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[i]), 0xB1, 0xF, 0xF, false));
-      v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ sgn);
-    }
-  }
+    // every lane's reads of the buffer have returned: refill it with the next chunk
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    store();
+    if (chunk + W < nchunks) issue(chunk + W);
 
-  const int64_t grow = row0 + lr;
-  if (lr >= nr) return;
-  uint8_t* crow = codes + grow * (D / 2) + half * 32;
-  uint8_t* srow = scales + grow * (D / 32) + half * 2;
-  uint8_t sb[2];
+    // in-lane butterflies h = 1, 2, 4, 8, 16, 32 (element index bits 0..5)
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    float* blk = v + 32 * b;
-    // integer max of |bits|: NaN and Inf sort above every finite value
-    uint32_t mh = 0;
+    for (int h = 1; h < 64; h *= 2) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mh = max(mh, absbits(blk[i]));
-#pragma unroll
-    for (int i = 0; i < 32; ++i) blk[i] = blk[i] * c;
-    uint32_t q[4] = {0u, 0u, 0u, 0u};
-    if (mh >= 0x7F800000u) {
-      sb[b] = 0xFF;
-    } else {
-      // max |fl(v c)| = fl(max|v| c), since rounding is monotone
-      const uint32_t mb = __float_as_uint(__uint_as_float(mh) * c);
-      const int e = mx_exponent(mb, rule);
-      quant32(blk, e, q);
-      sb[b] = (uint8_t)(e + 127);
+      for (int i = 0; i < 64; ++i) {
+        if ((i & h) == 0) {
+          const float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+      }
     }
-    *reinterpret_cast<uint4*>(crow + 16 * b) = make_uint4(q[0], q[1], q[2], q[3]);
+    if constexpr (LPR == 2) {
+      // h = 64: lane 2r holds elements 0..63 (the "a" side), lane 2r+1 holds 64..127.
+      // a-lane: own + partner = a + b;  b-lane: partner + (-own) = a - b.  The quad
+      // permute never leaves its quad, so every lane reads a partner and the move
+      // folds into the add as a DPP operand.
+      const uint32_t sgn = (uint32_t)half << 31;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float p = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[i]), 0xB1, 0xF, 0xF, true));
+        v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ sgn);
+      }
+    }
+
+    sb2 = 0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float* blk = v + 32 * b;
+      const uint32_t mh = absmax32_bits(blk);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) blk[i] = blk[i] * c;
+      q[b][0] = q[b][1] = q[b][2] = q[b][3] = 0u;
+      uint32_t sbyte = 0xFF;
+      if (mh < 0x7F800000u) {
+        // max |fl(v c)| = fl(max|v| c), since rounding is monotone
+        const uint32_t mb = __float_as_uint(__uint_as_float(mh) * c);
+        const int e = mx_exponent(mb, rule);
+        quant32(blk, e, q[b]);
+        sbyte = (uint32_t)(e + 127);
+      }
+      sb2 |= sbyte << (8 * b);
+    }
+    prow = chunk * G::RW + lr;
   }
-  *reinterpret_cast<uint16_t*>(srow) = (uint16_t)(sb[0] | (sb[1] << 8));
+  store();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) before the wave's LDS is released
 }
 
 // ---------------------------------------------------------------------------
@@ -168,9 +203,7 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
       v[4 * q + 2] = __uint_as_float(w.z); v[4 * q + 3] = __uint_as_float(w.w);
     }
   }
-  uint32_t mb = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) mb = max(mb, absbits(v[i]));
+  const uint32_t mb = absmax32_bits(v);
   uint32_t q[4] = {0u, 0u, 0u, 0u};
   uint8_t sb;
   if (mb >= 0x7F800000u) {
@@ -187,64 +220,75 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
 // ---------------------------------------------------------------------------
 // Quantise down the rows (tokens) and write transposed:
 //   x [batch, rows, cols] -> codes [batch, cols, P/2], scales [batch, cols, P/32].
-// A 256-thread block owns a tile of 128 tokens x 128 columns.  The tile is read
-// with coalesced dword loads into LDS (zero where rows >= `rows` or cols >=
-// `cols`), then thread t quantises columns (2p, 2p+1), p = t % 64, over the 32
-// tokens of block t / 64.  blockIdx.x: token tile; blockIdx.y: column tile;
-// blockIdx.z: batch.
+// A 256-thread block owns a tile of 256 tokens x 64 columns.  The tile is brought
+// into LDS by global->LDS DMA (16-byte units; tokens past `rows` read as zero through
+// the buffer descriptor's size), with unit q of token r stored at q ^ ((r / 32) % 8)
+// so that the column reads below spread over all banks.  Thread t then quantises
+// columns 2p, 2p + 1 (p = t / 8) over the 32 tokens of block t % 8: the eight lanes
+// of a column pair write the column's 128 code bytes of the tile contiguously.
+// blockIdx.x: token tile; blockIdx.y: column tile; blockIdx.z: batch.
+
 template <int EB>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t P,
                                                     uint8_t* __restrict__ codes,
                                                     uint8_t* __restrict__ scales, Rule rule) {
-  constexpr int TT = 128;                 // tokens per tile
-  constexpr int TC = 128;                 // columns per tile
-  constexpr int RB = TC * EB;             // bytes of one tile row
-  constexpr int STRIDE = RB + 4;          // dword padding
-  __shared__ __attribute__((aligned(16))) uint8_t tile[TT * STRIDE];
+  constexpr int TT = 256;         // tokens per tile
+  constexpr int TC = 64;          // columns per tile
+  constexpr int RB = TC * EB;     // bytes of one tile row: 128 (bf16) or 256 (fp32)
+  constexpr int CH = RB / 16;     // 16-byte units per tile row
+  constexpr int NDMA = TT * RB / 1024 / 4;  // 1 KB DMAs per wave
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TT * RB];
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t t0 = (int64_t)blockIdx.x * TT;
   const int64_t c0 = (int64_t)blockIdx.y * TC;
   const int64_t b = blockIdx.z;
-  const uint8_t* xb = x + b * rows * cols * EB;
-  // load: the tile is TT rows of RB bytes = TT * RB / 4 dwords
-  constexpr int NDW = TT * RB / 4;
-  constexpr int DW_PER_ROW = RB / 4;
-  const int64_t cbytes_valid = (cols - c0) * EB;  // bytes of valid columns in this tile row
-#pragma unroll 4
-  for (int k = tid; k < NDW; k += 256) {
-    const int r = k / DW_PER_ROW, q = k % DW_PER_ROW;
-    const int64_t tok = t0 + r;
-    uint32_t w = 0;
-    if (tok < rows && 4 * q < cbytes_valid)
-      w = *reinterpret_cast<const uint32_t*>(xb + (tok * cols + c0) * EB + 4 * q);
-    *reinterpret_cast<uint32_t*>(tile + r * STRIDE + 4 * q) = w;
+  {
+    // descriptor over this batch item from token t0, column c0 to its end
+    const int64_t left = ((rows - t0) * cols - c0) * EB;
+    const int n = left > 0x7FFFFFFF ? 0x7FFFFFFF : (int)left;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(x + ((b * rows + t0) * cols + c0) * EB), (short)0, n, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) {
+      const int slot = 64 * (NDMA * wave + u) + lane;  // 16-byte unit of the LDS tile
+      const int r = slot / CH, pos = slot % CH;
+      const int q = pos ^ (r >> 5);  // the global unit stored at `pos`
+      dma16(rs, tile + 1024 * (NDMA * wave + u), (uint32_t)(r * cols * EB + 16 * q));
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMAs have landed
   __syncthreads();
-  const int p = tid % 64, blk = tid / 64;
+
+  const int p = tid >> 3, blk = tid & 7;
+  const int sw = blk;  // (r / 32) % 8 for every token of this block
   float va[32], vb[32];
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const uint8_t* rp = tile + (32 * blk + k) * STRIDE + 2 * p * EB;
+    const int r = 32 * blk + k;
     if constexpr (EB == 2) {
-      uint32_t w = *reinterpret_cast<const uint32_t*>(rp);
+      // columns 2p, 2p+1: bytes 4p .. 4p+3 of the row, unit p / 4
+      const uint32_t w =
+          *reinterpret_cast<const uint32_t*>(tile + r * RB + 16 * ((p >> 2) ^ sw) + 4 * (p & 3));
       va[k] = bf16lo(w);
       vb[k] = bf16hi(w);
     } else {
-      uint2 w = *reinterpret_cast<const uint2*>(rp);
+      // bytes 8p .. 8p+7 of the row, unit p / 2
+      const uint2 w = *reinterpret_cast<const uint2*>(tile + r * RB + 16 * ((p >> 1) ^ sw) + 8 * (p & 1));
       va[k] = __uint_as_float(w.x);
       vb[k] = __uint_as_float(w.y);
     }
   }
   const int64_t col = c0 + 2 * p;
   const int64_t kv0 = t0 + 32 * blk;
+  if (kv0 >= P) return;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const float* v = s ? vb : va;
     if (col + s >= cols) break;
-    uint32_t mb = 0;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mb = max(mb, absbits(v[i]));
+    const uint32_t mb = absmax32_bits(v);
     uint32_t q[4] = {0u, 0u, 0u, 0u};
     uint8_t sb;
     if (mb >= 0x7F800000u) {
@@ -263,17 +307,22 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
 // ---------------------------------------------------------------------------
 hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, uint8_t* codes,
                                  uint8_t* scales, Rule rule, float c, hipStream_t s) {
-  const int rows_per_block = 256 / (d / 64);
-  const int64_t grid = (nrows + rows_per_block - 1) / rows_per_block;
+  const int rows_per_chunk = 64 / (d / 64);
+  const int64_t nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
+  // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (three
+  // per CU for bf16 input, two for fp32, by registers and LDS), each looping over chunks
+  int64_t grid = (nchunks + 3) / 4;
+  const int64_t resident = 256 * (eb == 2 ? 3 : 2);
+  if (grid > resident) grid = resident;
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   if (d == 128 && eb == 2)
-    hipLaunchKernelGGL((k_quant_hadamard<128, 2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c);
+    hipLaunchKernelGGL((k_quant_hadamard<128, 2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
   else if (d == 128 && eb == 4)
-    hipLaunchKernelGGL((k_quant_hadamard<128, 4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c);
+    hipLaunchKernelGGL((k_quant_hadamard<128, 4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
   else if (d == 64 && eb == 2)
-    hipLaunchKernelGGL((k_quant_hadamard<64, 2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c);
+    hipLaunchKernelGGL((k_quant_hadamard<64, 2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
   else if (d == 64 && eb == 4)
-    hipLaunchKernelGGL((k_quant_hadamard<64, 4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c);
+    hipLaunchKernelGGL((k_quant_hadamard<64, 4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -292,7 +341,7 @@ hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* co
 
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
                              int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, hipStream_t s) {
-  dim3 grid((unsigned)(P / 128), (unsigned)((cols + 127) / 128), (unsigned)batch);
+  dim3 grid((unsigned)((P + 255) / 256), (unsigned)((cols + 63) / 64), (unsigned)batch);
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   if (eb == 2)
     hipLaunchKernelGGL((k_quant_rows<2>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule);

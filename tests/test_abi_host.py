@@ -16,8 +16,8 @@ HEADER = os.path.join(ROOT, "include", "mxattn.h")
 def mx():
     lib = os.path.join(ROOT, "mxfp4_bit_attention_amd", "libmxattn.so")
     if not os.path.exists(lib):
-        from mxfp4_bit_attention_amd import build
-        build.build()
+        import __graft_entry__
+        __graft_entry__.build()
     import mxfp4_bit_attention_amd as m
     return m
 
@@ -77,6 +77,7 @@ def q_call(mx, x=FAKE, dtype=1, batch=1, rows=4, cols=128, axis=0, kind=0, qmax=
     (dict(axis=5), -1, "axis"),
     (dict(axis=1, had=1), -1, "Hadamard"),
     (dict(axis=1, cols=7), -1, "even"),
+    (dict(axis=1, cols=1 << 17), -1, "cols <= 65536"),
     (dict(kind=9), -1, "rule"),
     (dict(kind=2, qmax=3.0), -1, "(4, 8]"),
     (dict(kind=2, qmax=float("nan")), -1, "(4, 8]"),
