@@ -14,10 +14,14 @@ Printed as one JSON line, with:
                  was taken on the current kernel source (else null);
   quantize_pass  the standalone Hadamard + quantise pass on 40 x 75,600 x 128
                  bf16 against HBM bandwidth (UOS, OCP and q = 6);
+  rule_ablation  the full step under each shared-exponent rule (UOS, OCP, TFS,
+                 OAS and CEIL 7.5; the same rule for Q, K, V and P~);
+  other_shapes   the full step at d = 64, at B = 2 x H = 20, and with 512 keys
+                 (cross-attention-like);
   cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
                  on this host, extrapolated to the full workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-extras]
     python bench.py --traffic-probe     (one copy of known size + one attention
                                          launch, for rocprofv3 --pmc runs)
 """
@@ -26,6 +30,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -137,6 +142,48 @@ def cpu_baseline(w) -> dict:
     }
 
 
+# Shared-exponent rules of the ablation: UOS (CEIL 7.25), OCP floor, TFS (CEIL 6), OAS (CEIL 7)
+# and CEIL 7.5 (Pith review of MXAttention, referee report: the missing Qmax sweep).
+ABLATION_RULES = (("uos", "uos"), ("ocp", "ocp"), ("tfs_q6", ("ceil", 6.0)), ("oas_q7", ("ceil", 7.0)),
+                  ("q7.5", ("ceil", 7.5)))
+
+
+def extras(torch, mx, w, q, k, v, out, ws, stream, iters: int = 5) -> dict:
+    """Scale-rule ablation of the full step at the headline shape (the same rule for
+    Q, K, V and the P~ tiles), and the step at other shapes the boundary takes: d = 64,
+    two batch entries, and a short key sequence (text-like cross-attention)."""
+    res = {}
+    ab = {}
+    for name, rule in ABLATION_RULES:
+        fn = lambda rule=rule: mx.mxattn_forward(q, k, v, float(w.softmax_scale), hadamard=True, pnq=True,
+                                                 rule=rule, out=out, workspace=ws)
+        fn()
+        ms = time_launches(torch, fn, iters, stream)
+        ab[name] = {"ms_per_step": round(ms, 3), "TFLOPs": round(w.flops / (ms * 1e-3) / 1e12, 1)}
+    res["rule_ablation"] = {"workload": w.name, "pnq": True, "hadamard": True, "rules": ab}
+
+    shapes = {}
+    other = (("d64", dict(B=1, H=40, Nq=w.N, Nkv=w.N, d=64)),
+             ("B2_H20", dict(B=2, H=20, Nq=w.N, Nkv=w.N, d=128)),
+             ("cross_Nkv512", dict(B=1, H=40, Nq=w.N, Nkv=512, d=128)))
+    for name, sh in other:
+        g = torch.Generator(device=q.device).manual_seed(7)
+        mk = lambda n: torch.randn((sh["B"], sh["H"], n, sh["d"]), generator=g, device=q.device).to(torch.bfloat16)
+        qq, kk, vv = mk(sh["Nq"]), mk(sh["Nkv"]), mk(sh["Nkv"])
+        oo = torch.empty_like(qq)
+        wsz = mx.mxattn_forward_workspace_bytes(sh["B"], sh["H"], sh["Nq"], sh["Nkv"], sh["d"])
+        wws = torch.empty(wsz, dtype=torch.uint8, device=q.device)
+        sc = 1.0 / math.sqrt(sh["d"])
+        fn = lambda: mx.mxattn_forward(qq, kk, vv, sc, hadamard=True, pnq=True, rule="uos", out=oo, workspace=wws)
+        fn()
+        ms = time_launches(torch, fn, iters, stream)
+        flops = 4.0 * sh["B"] * sh["H"] * sh["Nq"] * sh["Nkv"] * sh["d"]
+        shapes[name] = dict(sh, ms_per_step=round(ms, 3), TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1))
+        del qq, kk, vv, oo, wws
+    res["other_shapes"] = shapes
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +192,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-pass", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the scale-rule ablation and the other-shape lines")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path runs on a single MI355X); got --gpus {args.gpus}",
@@ -245,6 +294,10 @@ def main():
             qp[name] = {"us": round(ms * 1e3, 1), "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
         result["quantize_pass"] = qp
         del x, c, s
+
+    if not args.no_extras:
+        result.update(extras(torch, mx, w, q, k, v, out, ws, stream))
+    del q, k, v, out, ws
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)

@@ -54,4 +54,4 @@ def p_code_mismatch(gpu_pc_packed: np.ndarray, gpu_ps: np.ndarray, ora_pc: np.nd
 
 
 RULES = {"uos": ("uos", mxfp4.UOS), "ocp": ("ocp", mxfp4.OCP), "tfs": (("ceil", 6.0), mxfp4.TFS),
-         "oas": (("ceil", 7.0), mxfp4.OAS)}
+         "oas": (("ceil", 7.0), mxfp4.OAS), "q7.5": (("ceil", 7.5), ("ceil", 7.5))}

@@ -80,6 +80,36 @@ def test_quantized_entry_p_codes(rule, Nq, Nkv, d):
     assert mm < P_MISMATCH, f"P^ code mismatch {mm:.2e}"
 
 
+@pytest.mark.parametrize("rule", ["oas", "q7.5"])
+@pytest.mark.parametrize("Nq,Nkv,d", [(300, 1000, 128), (64, 33, 64)])
+def test_ablation_rules_p_codes(rule, Nq, Nkv, d):
+    """The other CEIL rules of the scale-rule ablation (q = 7 and 7.5) on the P~ tiles."""
+    test_quantized_entry_p_codes(rule, Nq, Nkv, d)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,d,dtype", [(2, 2, 300, 700, 128, "bf16"), (3, 1, 129, 257, 64, "f32")])
+def test_batched_cross_shape_pipeline(B, H, Nq, Nkv, d, dtype):
+    """B > 1 and N_q != N_kv through mxattn_forward (Hadamard, UOS, PNQ); every row of
+    every (batch, head) against the oracle pipeline."""
+    torch, mx = require_gpu()
+    rng = np.random.default_rng(B * 1000 + Nq + Nkv + d)
+    Q = rng.standard_normal((B, H, Nq, d)).astype(np.float32)
+    K = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    if dtype == "bf16":
+        Q, K, V = (synth.bf16_to_f32(synth.round_to_bf16(a)) for a in (Q, K, V))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    O = mx.mxattn_forward(*(to_device(a, dtype) for a in (Q, K, V)), scale, hadamard=True, pnq=True, rule="uos")
+    torch.cuda.synchronize()
+    Og = O.float().cpu().numpy()
+    Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(Nkv)
+    for b in range(B):
+        for h in range(H):
+            Oo = ora.mx_attention_pipeline(Q[b, h], K[b, h], V[b, h], scale, True, True, mxfp4.UOS, Bc, P)
+            err = rel_l2(Og[b, h], Oo)
+            assert err < REL_L2, f"batch {b} head {h}: rel-L2 {err:.2e}"
+
+
 @pytest.mark.parametrize("rule", ["uos", "ocp", "tfs"])
 def test_pnq_sum_to_one_on_gpu(rule):
     """V = 1: PNQ gives O = 1 within 1e-6; direct placement visibly does not."""
