@@ -104,6 +104,25 @@ int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, i
                     int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
                     uint8_t* codes, uint8_t* scales, void* stream);
 
+/*
+ * mxattn_quant_error -- the quantisation error of mxattn_quantize, for the scale-rule
+ * (Qmax) sweep that the Pith review's referee report asks for (major comments: the
+ * optimality of q = 7.25 is argued for a model density, per-block sweeps on real
+ * tensors, P~ tiles included, are missing).  Same arguments and checks as
+ * mxattn_quantize, but nothing is stored: the blocks are quantised exactly as
+ * mxattn_quantize would (after the Hadamard rotation when hadamard != 0), each code
+ * is dequantised, and
+ *   sums[0] = sum over finite blocks of (value - dequantised value)^2,
+ *   sums[1] = sum over finite blocks of value^2,
+ *   sums[2] = number of blocks left out because they hold Inf or NaN,
+ * where "value" is what was quantised (the rotated fp32 value with hadamard != 0).
+ * sums: 3 doubles of device memory, 8-byte aligned, owned by the caller; the call
+ * zeroes them on `stream` before adding.  Per-block sums are fp32, the totals fp64.
+ */
+int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols,
+                       int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
+                       double* sums, void* stream);
+
 /* Bytes of workspace mxattn_forward needs: the quantised Q, K (along d) and the
  * transposed quantised V (along tokens), each piece 256-byte aligned.  Returns 0
  * for invalid sizes. */

@@ -6,7 +6,7 @@ PyTorch supplies device memory and the current stream.  The library must be
 built first (``python mxfp4_bit_attention_amd/build.py``); importing this
 module raises if it is missing, and nothing here falls back to a CPU path.
 
-Names mirror the C entry points: ``mxattn_quantize``, ``mxattn_forward``,
+Names mirror the C entry points: ``mxattn_quantize``, ``mxattn_quant_error``, ``mxattn_forward``,
 ``mxattn_forward_quantized``, ``mxattn_forward_workspace_bytes``,
 ``mxattn_kv_tile``, ``mxattn_padded_tokens``, ``mxattn_last_error``.
 Rules are given as ``"uos"``, ``"ocp"`` or ``("ceil", q)``.
@@ -30,7 +30,7 @@ MXATTN_AXIS_LAST, MXATTN_AXIS_ROWS = 0, 1
 
 EXPORTED = (
     "mxattn_kv_tile", "mxattn_padded_tokens", "mxattn_quantize", "mxattn_forward_workspace_bytes",
-    "mxattn_forward", "mxattn_forward_quantized", "mxattn_last_error",
+    "mxattn_forward", "mxattn_forward_quantized", "mxattn_last_error", "mxattn_quant_error",
 )
 
 
@@ -54,6 +54,8 @@ def _load() -> ctypes.CDLL:
     lib.mxattn_last_error.argtypes = []
     lib.mxattn_quantize.restype = c.c_int
     lib.mxattn_quantize.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, u32, vp, vp, vp]
+    lib.mxattn_quant_error.restype = c.c_int
+    lib.mxattn_quant_error.argtypes = [vp, i32, i64, i64, i64, i32, i32, f32, u32, vp, vp]
     lib.mxattn_forward_workspace_bytes.restype = sz
     lib.mxattn_forward_workspace_bytes.argtypes = [i64, i64, i64, i64, i64]
     lib.mxattn_forward.restype = c.c_int
@@ -64,6 +66,10 @@ def _load() -> ctypes.CDLL:
                                              i32, f32, vp, i32, vp, vp, vp]
     return lib
 
+
+# torch first: libmxattn then binds to the HIP runtime torch already loaded, so
+# tensors, streams and the kernels share one runtime whatever the import order
+import torch  # noqa: E402,F401
 
 LIB = _load()
 
@@ -167,6 +173,31 @@ def mxattn_quantize(x, rule="uos", axis: str = "last", hadamard: bool = False, c
     if squeeze:
         return codes[0], scales[0]
     return codes, scales
+
+
+def mxattn_quant_error(x, rule="uos", axis: str = "last", hadamard: bool = False, sums=None):
+    """Quantisation error of mxattn_quantize(x, rule, axis, hadamard) without storing codes.
+
+    Returns a float64 device tensor [3]: sum (value - dequantised)^2 and sum value^2 over
+    finite blocks, and the number of non-finite blocks (values are the rotated ones
+    when hadamard is set).
+    """
+    torch = _torch()
+    _need_cuda(x)
+    x3 = x.unsqueeze(0) if x.dim() == 2 else x
+    if x3.dim() != 3:
+        raise ValueError("x must be 2-D or 3-D")
+    b, r, c = x3.shape
+    ax = {"last": MXATTN_AXIS_LAST, "rows": MXATTN_AXIS_ROWS}.get(axis)
+    if ax is None:
+        raise ValueError("axis must be 'last' or 'rows'")
+    if sums is None:
+        sums = torch.empty(3, dtype=torch.float64, device=x.device)
+    _need_cuda(sums)
+    kind, q = rule_args(rule)
+    _check(LIB.mxattn_quant_error(_ptr(x3), _dtype_code(x3), b, r, c, ax, kind, q, int(bool(hadamard)),
+                                  _ptr(sums), _stream(x.device)))
+    return sums
 
 
 def mxattn_forward(q, k, v, softmax_scale: float, hadamard: bool = True, pnq: bool = True, rule="uos",

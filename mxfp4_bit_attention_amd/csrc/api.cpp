@@ -142,15 +142,22 @@ int64_t mxattn_padded_tokens(int64_t n) { return n < 0 ? -1 : round_up(n, mxattn
 
 const char* mxattn_last_error(void) { return g_err.c_str(); }
 
-int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols,
-                    int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
-                    uint8_t* codes, uint8_t* scales, void* stream) {
-  const char* who = "mxattn_quantize";
+}  // extern "C"
+
+namespace {
+
+// Shared by mxattn_quantize (err == nullptr: store codes and scales) and
+// mxattn_quant_error (err != nullptr: store nothing, sum the quantisation error).
+int quantize_impl(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols, int32_t axis,
+                  int32_t rule_kind, float qmax, uint32_t hadamard, uint8_t* codes, uint8_t* scales, double* err,
+                  void* stream, const char* who) {
   const int eb = elem_bytes(dtype);
   if (!eb) return fail(MXATTN_E_INVALID, "%s: dtype must be MXATTN_F32 or MXATTN_BF16", who);
-  if (!x || !codes || !scales) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
-  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+  if (!x || (!err && (!codes || !scales))) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if (!aligned16(x) || (!err && (!aligned16(codes) || !aligned16(scales))))
     return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if (err && (reinterpret_cast<uintptr_t>(err) & 7))
+    return fail(MXATTN_E_INVALID, "%s: sums must be 8-byte aligned", who);
   if (batch < 1 || rows < 1 || cols < 1)
     return fail(MXATTN_E_INVALID, "%s: batch, rows, cols must be >= 1", who);
   int64_t n;
@@ -158,30 +165,51 @@ int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, i
   mxattn::Rule rule{};
   if (int st = make_rule(rule_kind, qmax, &rule, who)) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
   if (axis == MXATTN_AXIS_LAST) {
     if (cols % 32) return fail(MXATTN_E_INVALID, "%s: cols must be a multiple of 32 for AXIS_LAST", who);
-    if (hadamard) {
-      if (cols != 64 && cols != 128)
-        return fail(MXATTN_E_UNSUPPORTED, "%s: the Hadamard rotation supports cols 64 or 128, got %lld", who,
-                    (long long)cols);
-      e = mxattn::launch_quant_hadamard(x, eb, (int)cols, batch * rows, codes, scales, rule,
-                                        inv_sqrt_f32((int)cols), s);
-    } else {
-      e = mxattn::launch_quant_last(x, eb, n / 32, codes, scales, rule, s);
-    }
+    if (hadamard && cols != 64 && cols != 128)
+      return fail(MXATTN_E_UNSUPPORTED, "%s: the Hadamard rotation supports cols 64 or 128, got %lld", who,
+                  (long long)cols);
   } else if (axis == MXATTN_AXIS_ROWS) {
     if (hadamard) return fail(MXATTN_E_INVALID, "%s: AXIS_ROWS does not take a Hadamard rotation", who);
     if (cols % 2) return fail(MXATTN_E_INVALID, "%s: cols must be even for AXIS_ROWS", who);
     if (batch > 65535 || cols > 65536)
       return fail(MXATTN_E_INVALID, "%s: AXIS_ROWS needs batch <= 65535 and cols <= 65536", who);
-    const int64_t P = round_up(rows, mxattn::kKvTile);
-    e = mxattn::launch_quant_rows(x, eb, batch, rows, cols, P, codes, scales, rule, s);
   } else {
     return fail(MXATTN_E_INVALID, "%s: axis must be MXATTN_AXIS_LAST or MXATTN_AXIS_ROWS", who);
   }
+  hipError_t e = hipSuccess;
+  if (err) e = hipMemsetAsync(err, 0, 3 * sizeof(double), s);
+  if (e == hipSuccess) {
+    if (axis == MXATTN_AXIS_LAST && hadamard)
+      e = mxattn::launch_quant_hadamard(x, eb, (int)cols, batch * rows, codes, scales, rule, inv_sqrt_f32((int)cols),
+                                        err, s);
+    else if (axis == MXATTN_AXIS_LAST)
+      e = mxattn::launch_quant_last(x, eb, n / 32, codes, scales, rule, err, s);
+    else
+      e = mxattn::launch_quant_rows(x, eb, batch, rows, cols, round_up(rows, mxattn::kKvTile), codes, scales, rule,
+                                    err, s);
+  }
   if (e != hipSuccess) return hip_fail(e, who);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols,
+                    int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
+                    uint8_t* codes, uint8_t* scales, void* stream) {
+  return quantize_impl(x, dtype, batch, rows, cols, axis, rule_kind, qmax, hadamard, codes, scales, nullptr, stream,
+                       "mxattn_quantize");
+}
+
+int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols, int32_t axis,
+                       int32_t rule_kind, float qmax, uint32_t hadamard, double* sums, void* stream) {
+  if (!sums) return fail(MXATTN_E_INVALID, "mxattn_quant_error: null pointer");
+  return quantize_impl(x, dtype, batch, rows, cols, axis, rule_kind, qmax, hadamard, nullptr, nullptr, sums, stream,
+                       "mxattn_quant_error");
 }
 
 size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d) {
@@ -263,13 +291,13 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, i
   hipError_t e;
   if (hadamard) {
     const float c = inv_sqrt_f32((int)d);
-    e = mxattn::launch_quant_hadamard(Q, eb, (int)d, B * H * Nq, qc, qs, rule, c, s);
-    if (e == hipSuccess) e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ks, rule, c, s);
+    e = mxattn::launch_quant_hadamard(Q, eb, (int)d, B * H * Nq, qc, qs, rule, c, nullptr, s);
+    if (e == hipSuccess) e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ks, rule, c, nullptr, s);
   } else {
-    e = mxattn::launch_quant_last(Q, eb, B * H * Nq * d / 32, qc, qs, rule, s);
-    if (e == hipSuccess) e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, s);
+    e = mxattn::launch_quant_last(Q, eb, B * H * Nq * d / 32, qc, qs, rule, nullptr, s);
+    if (e == hipSuccess) e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, nullptr, s);
   }
-  if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vs, rule, s);
+  if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vs, rule, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, who);
   return attention_core(qc, qs, kc, ks, vc, vs, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O, dtype, nullptr,
                         nullptr, s, who);

@@ -16,15 +16,17 @@ struct Rule {
   uint32_t q_frac;
 };
 
+// Quantisers.  With err == nullptr they store codes and scales; with err != nullptr
+// they store nothing and add {sum (x - dequant)^2, sum x^2, non-finite blocks} to err[0..2].
 // Fused Hadamard + quantise along the last axis; d in {64, 128}; eb = 2 (bf16) or 4 (fp32).
 hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, uint8_t* codes,
-                                 uint8_t* scales, Rule rule, float c, hipStream_t s);
+                                 uint8_t* scales, Rule rule, float c, double* err, hipStream_t s);
 // Quantise along the last axis in 32-element blocks (nblocks blocks, contiguous).
 hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* codes, uint8_t* scales,
-                             Rule rule, hipStream_t s);
+                             Rule rule, double* err, hipStream_t s);
 // Quantise down the rows, transposed output with P (multiple of 128) padded tokens.
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
-                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, hipStream_t s);
+                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s);
 
 struct AttnArgs {
   const uint8_t* qc;

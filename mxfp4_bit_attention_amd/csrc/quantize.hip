@@ -21,6 +21,50 @@
 
 namespace mxattn {
 
+// Quantisation error of a lane's blocks, for the Qmax-sweep diagnostic (no codes are
+// stored in that mode): the sum of squared differences between the values that were
+// quantised and their dequantised codes, the sum of squared values, and the number of
+// blocks left out as non-finite.  Per-block sums are fp32, the running sums fp64.
+struct ErrAcc {
+  double e2 = 0.0, r2 = 0.0, nf = 0.0;
+  __device__ __forceinline__ void add(const float* v, const uint32_t (&q)[4], int e) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const float s = e8m0_scale(e);
+    float se = 0.0f, sr = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      v2f d[4];
+      d[0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], s, 0);
+      d[1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], s, 1);
+      d[2] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], s, 2);
+      d[3] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(q[w], s, 3);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float a0 = v[8 * w + 2 * b], a1 = v[8 * w + 2 * b + 1];
+        const float d0 = a0 - d[b].x, d1 = a1 - d[b].y;
+        se += d0 * d0 + d1 * d1;
+        sr += a0 * a0 + a1 * a1;
+      }
+    }
+    e2 += se;
+    r2 += sr;
+  }
+  // sum over the wave, then one atomic add per wave into out[0..2]
+  __device__ __forceinline__ void flush(double* out) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      e2 += __shfl_xor(e2, m);
+      r2 += __shfl_xor(r2, m);
+      nf += __shfl_xor(nf, m);
+    }
+    if ((threadIdx.x & 63) == 0) {
+      atomicAdd(out + 0, e2);
+      atomicAdd(out + 1, r2);
+      atomicAdd(out + 2, nf);
+    }
+  }
+};
+
 
 // ---------------------------------------------------------------------------
 // Fused Hadamard + quantise.  D in {64, 128}; EB = bytes per input element (2 = bf16, 4 = fp32).
@@ -50,11 +94,11 @@ struct HadGeo {
   }
 };
 
-template <int D, int EB>
+template <int D, int EB, bool ERR>
 __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restrict__ x, int64_t nrows,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales, Rule rule,
-                                                        float c, int64_t nchunks) {
+                                                        float c, int64_t nchunks, double* err) {
   using G = HadGeo<D, EB>;
   constexpr int LPR = G::LPR;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::NW * G::CB];
@@ -92,8 +136,9 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
   uint32_t q[2][4];
   uint32_t sb2 = 0;
   int64_t prow = -1;  // row whose results q / sb2 hold (-1: none)
+  ErrAcc acc;
   auto store = [&]() {
-    if (prow >= 0 && prow < nrows) {
+    if (!ERR && prow >= 0 && prow < nrows) {
       uint8_t* crow = codes + prow * (D / 2) + half * 32;
       *reinterpret_cast<uint4*>(crow) = make_uint4(q[0][0], q[0][1], q[0][2], q[0][3]);
       *reinterpret_cast<uint4*>(crow + 16) = make_uint4(q[1][0], q[1][1], q[1][2], q[1][3]);
@@ -167,23 +212,29 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
         const int e = mx_exponent(mb, rule);
         quant32(blk, e, q[b]);
         sbyte = (uint32_t)(e + 127);
+        if (ERR && chunk * G::RW + lr < nrows) acc.add(blk, q[b], e);
+      } else if (ERR && chunk * G::RW + lr < nrows) {
+        acc.nf += 1.0;
       }
       sb2 |= sbyte << (8 * b);
     }
     prow = chunk * G::RW + lr;
   }
   store();
+  if constexpr (ERR) acc.flush(err);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) before the wave's LDS is released
 }
 
 // ---------------------------------------------------------------------------
 // Plain quantise along the last axis: one thread per 32-element block.
-template <int EB>
+template <int EB, bool ERR>
 __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ x, int64_t nblocks,
                                                     uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, Rule rule) {
-  const int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (blk >= nblocks) return;
+                                                    uint8_t* __restrict__ scales, Rule rule, double* err) {
+  const int64_t blk0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (!ERR && blk0 >= nblocks) return;
+  const bool valid = blk0 < nblocks;
+  const int64_t blk = valid ? blk0 : nblocks - 1;
   float v[32];
   const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32 * EB);
   if constexpr (EB == 2) {
@@ -206,15 +257,22 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
   const uint32_t mb = absmax32_bits(v);
   uint32_t q[4] = {0u, 0u, 0u, 0u};
   uint8_t sb;
+  ErrAcc acc;
   if (mb >= 0x7F800000u) {
     sb = 0xFF;
+    if (ERR && valid) acc.nf = 1.0;
   } else {
     const int e = mx_exponent(mb, rule);
     quant32(v, e, q);
     sb = (uint8_t)(e + 127);
+    if (ERR && valid) acc.add(v, q, e);
   }
-  *reinterpret_cast<uint4*>(codes + blk * 16) = make_uint4(q[0], q[1], q[2], q[3]);
-  scales[blk] = sb;
+  if constexpr (ERR) {
+    acc.flush(err);
+  } else {
+    *reinterpret_cast<uint4*>(codes + blk * 16) = make_uint4(q[0], q[1], q[2], q[3]);
+    scales[blk] = sb;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -228,11 +286,11 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
 // of a column pair write the column's 128 code bytes of the tile contiguously.
 // blockIdx.x: token tile; blockIdx.y: column tile; blockIdx.z: batch.
 
-template <int EB>
+template <int EB, bool ERR>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t P,
                                                     uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, Rule rule) {
+                                                    uint8_t* __restrict__ scales, Rule rule, double* err) {
   constexpr int TT = 256;         // tokens per tile
   constexpr int TC = 64;          // columns per tile
   constexpr int RB = TC * EB;     // bytes of one tile row: 128 (bf16) or 256 (fp32)
@@ -283,30 +341,45 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
   }
   const int64_t col = c0 + 2 * p;
   const int64_t kv0 = t0 + 32 * blk;
-  if (kv0 >= P) return;
+  if (!ERR && kv0 >= P) return;
+  ErrAcc acc;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const float* v = s ? vb : va;
-    if (col + s >= cols) break;
+    if (kv0 >= P || col + s >= cols) break;
     const uint32_t mb = absmax32_bits(v);
     uint32_t q[4] = {0u, 0u, 0u, 0u};
     uint8_t sb;
     if (mb >= 0x7F800000u) {
       sb = 0xFF;
+      if (ERR) acc.nf += 1.0;
     } else {
       const int e = mx_exponent(mb, rule);
       quant32(v, e, q);
       sb = (uint8_t)(e + 127);
+      if (ERR) acc.add(v, q, e);
     }
-    const int64_t crow = b * cols + col + s;
-    *reinterpret_cast<uint4*>(codes + crow * (P / 2) + kv0 / 2) = make_uint4(q[0], q[1], q[2], q[3]);
-    scales[crow * (P / 32) + kv0 / 32] = sb;
+    if constexpr (!ERR) {
+      const int64_t crow = b * cols + col + s;
+      *reinterpret_cast<uint4*>(codes + crow * (P / 2) + kv0 / 2) = make_uint4(q[0], q[1], q[2], q[3]);
+      scales[crow * (P / 32) + kv0 / 32] = sb;
+    }
   }
+  if constexpr (ERR) acc.flush(err);
 }
 
 // ---------------------------------------------------------------------------
+// Launchers.  With err == nullptr the kernels store codes and scales; otherwise they
+// store nothing and add the quantisation error sums to err[0..2] (the Qmax sweep).
+template <int D, int EB, bool ERR>
+static void launch_h(unsigned grid, const uint8_t* x, int64_t nrows, uint8_t* codes, uint8_t* scales, Rule rule,
+                     float c, int64_t nchunks, double* err, hipStream_t s) {
+  hipLaunchKernelGGL((k_quant_hadamard<D, EB, ERR>), dim3(grid), dim3(256), 0, s, x, nrows, codes, scales, rule, c,
+                     nchunks, err);
+}
+
 hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, uint8_t* codes,
-                                 uint8_t* scales, Rule rule, float c, hipStream_t s) {
+                                 uint8_t* scales, Rule rule, float c, double* err, hipStream_t s) {
   const int rows_per_chunk = 64 / (d / 64);
   const int64_t nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
   // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (three
@@ -315,38 +388,45 @@ hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, ui
   const int64_t resident = 256 * (eb == 2 ? 3 : 2);
   if (grid > resident) grid = resident;
   const uint8_t* xp = static_cast<const uint8_t*>(x);
-  if (d == 128 && eb == 2)
-    hipLaunchKernelGGL((k_quant_hadamard<128, 2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
-  else if (d == 128 && eb == 4)
-    hipLaunchKernelGGL((k_quant_hadamard<128, 4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
-  else if (d == 64 && eb == 2)
-    hipLaunchKernelGGL((k_quant_hadamard<64, 2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
-  else if (d == 64 && eb == 4)
-    hipLaunchKernelGGL((k_quant_hadamard<64, 4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nrows, codes, scales, rule, c, nchunks);
+  const unsigned g = (unsigned)grid;
+  const bool e = err != nullptr;
+  if (d == 128 && eb == 2) e ? launch_h<128, 2, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
+                             : launch_h<128, 2, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
+  else if (d == 128 && eb == 4) e ? launch_h<128, 4, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
+                                  : launch_h<128, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
+  else if (d == 64 && eb == 2) e ? launch_h<64, 2, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
+                                 : launch_h<64, 2, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
+  else if (d == 64 && eb == 4) e ? launch_h<64, 4, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
+                                 : launch_h<64, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* codes, uint8_t* scales,
-                             Rule rule, hipStream_t s) {
+                             Rule rule, double* err, hipStream_t s) {
   const int64_t grid = (nblocks + 255) / 256;
   const uint8_t* xp = static_cast<const uint8_t*>(x);
-  if (eb == 2)
-    hipLaunchKernelGGL((k_quant_last<2>), dim3((unsigned)grid), dim3(256), 0, s, xp, nblocks, codes, scales, rule);
-  else
-    hipLaunchKernelGGL((k_quant_last<4>), dim3((unsigned)grid), dim3(256), 0, s, xp, nblocks, codes, scales, rule);
+  const dim3 g((unsigned)grid), b(256);
+  if (eb == 2 && err) hipLaunchKernelGGL((k_quant_last<2, true>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
+  else if (eb == 2) hipLaunchKernelGGL((k_quant_last<2, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
+  else if (err) hipLaunchKernelGGL((k_quant_last<4, true>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
+  else hipLaunchKernelGGL((k_quant_last<4, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
-                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, hipStream_t s) {
+                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s) {
   dim3 grid((unsigned)((P + 255) / 256), (unsigned)((cols + 63) / 64), (unsigned)batch);
   const uint8_t* xp = static_cast<const uint8_t*>(x);
-  if (eb == 2)
-    hipLaunchKernelGGL((k_quant_rows<2>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule);
+  if (eb == 2 && err)
+    hipLaunchKernelGGL((k_quant_rows<2, true>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
+  else if (eb == 2)
+    hipLaunchKernelGGL((k_quant_rows<2, false>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
+  else if (err)
+    hipLaunchKernelGGL((k_quant_rows<4, true>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
   else
-    hipLaunchKernelGGL((k_quant_rows<4>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule);
+    hipLaunchKernelGGL((k_quant_rows<4, false>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
   return hipGetLastError();
 }
 

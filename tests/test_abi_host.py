@@ -116,6 +116,18 @@ def test_forward_rejects_bad_arguments(mx, kw, status, msg):
     assert msg in mx.mxattn_last_error()
 
 
+def test_quant_error_rejects_bad_arguments(mx):
+    p = ctypes.c_void_p
+    L = mx.LIB
+    assert L.mxattn_quant_error(p(FAKE), 1, 1, 4, 128, 0, 0, 7.25, 0, None, None) == -1
+    assert "null" in mx.mxattn_last_error()
+    assert L.mxattn_quant_error(p(FAKE), 1, 1, 4, 128, 0, 0, 7.25, 0, p(FAKE + 4), None) == -1
+    assert "8-byte" in mx.mxattn_last_error()
+    assert L.mxattn_quant_error(p(FAKE), 1, 1, 4, 96, 0, 0, 7.25, 1, p(FAKE), None) == -2
+    assert L.mxattn_quant_error(p(FAKE), 1, 1, 4, 128, 1, 0, 7.25, 1, p(FAKE), None) == -1
+    assert "Hadamard" in mx.mxattn_last_error()
+
+
 def test_forward_quantized_rejects_bad_arguments(mx):
     p = ctypes.c_void_p
     L = mx.LIB
