@@ -123,15 +123,18 @@ int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows
                        int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
                        double* sums, void* stream);
 
-/* Bytes of workspace mxattn_forward needs: the quantised Q, K (along d) and the
- * transposed quantised V (along tokens), each piece 256-byte aligned.  Returns 0
+/* Bytes of workspace mxattn_forward needs: the quantised K (along d) and the
+ * transposed quantised V (along tokens), each piece 256-byte aligned (Q is
+ * rotated and quantised inside the attention kernel and never stored).  Returns 0
  * for invalid sizes. */
 size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d);
 
 /*
  * mxattn_forward -- MXFP4 attention forward, O = softmax(scale Q K^T) V, with
  * the MXAttention pipeline (Pith review, Figure 1 caption and Figure 4; abstract):
- *   1. Q and K: optional Hadamard rotation along d, then block quantisation along d.
+ *   1. Q and K: optional Hadamard rotation along d, then block quantisation along d
+ *      (K by the quantiser into the workspace; Q by the attention kernel as it loads
+ *      its query rows -- the same arithmetic, so the same codes as mxattn_quantize).
  *   2. V: block quantisation along tokens.
  *   3. FlashAttention-2 online softmax over kv tiles of mxattn_kv_tile() keys, in
  *      increasing order.  Per tile: S = scale * (Q^ K^^T) on block-scaled MFMA;

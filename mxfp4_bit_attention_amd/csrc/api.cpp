@@ -95,16 +95,15 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t qc, qs, kc, ks, vc, vs, total;
+  size_t kc, ks, vc, vs, total;
 };
 
+// The forward's workspace: K^ and V^T (Q is quantised inside the attention kernel).
 bool fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, FwdLayout* L) {
   int64_t nq_e, nkv_e, v_e;
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
   if (!elems(B, H, Nq, d, &nq_e) || !elems(B, H, Nkv, d, &nkv_e) || !elems(B, H, P, d, &v_e)) return false;
   Carve c;
-  L->qc = c.take((size_t)nq_e / 2);
-  L->qs = c.take((size_t)nq_e / 32);
   L->kc = c.take((size_t)nkv_e / 2);
   L->ks = c.take((size_t)nkv_e / 32);
   L->vc = c.take((size_t)v_e / 2);
@@ -219,11 +218,19 @@ size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t 
   return L.total;
 }
 
+// Raw Q for the fused quantisation in the attention kernel's prologue.
+struct QuantQ {
+  const void* q;
+  bool bf16;
+  bool hadamard;
+  float c;
+};
+
 static int attention_core(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ks,
                           const uint8_t* VTc, const uint8_t* VTs, int64_t B, int64_t H, int64_t Nq,
                           int64_t Nkv, int64_t d, float softmax_scale, uint32_t pnq,
                           const mxattn::Rule& pr, void* O, int32_t out_dtype, uint8_t* pc, uint8_t* ps,
-                          hipStream_t s, const char* who) {
+                          hipStream_t s, const char* who, const QuantQ* fused = nullptr) {
   mxattn::AttnArgs a{};
   a.qc = Qc;
   a.qs = Qs;
@@ -240,6 +247,12 @@ static int attention_core(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* K
   a.kv_pad = round_up(Nkv, mxattn::kKvTile);
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   a.out_bf16 = out_dtype == MXATTN_BF16;
+  if (fused) {
+    a.qraw = fused->q;
+    a.q_bf16 = fused->bf16 ? 1 : 0;
+    a.q_hadamard = fused->hadamard ? 1 : 0;
+    a.q_c = fused->c;
+  }
   hipError_t e = mxattn::launch_attention(a, (int)d, pnq ? 1 : 0, pr, s);
   if (e != hipSuccess) return hip_fail(e, who);
   return ok();
@@ -285,22 +298,21 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, i
   if (workspace_bytes < L.total)
     return fail(MXATTN_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, workspace_bytes, L.total);
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  uint8_t *qc = w + L.qc, *qs = w + L.qs, *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs;
+  uint8_t *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
+  const float c = inv_sqrt_f32((int)d);
   hipError_t e;
-  if (hadamard) {
-    const float c = inv_sqrt_f32((int)d);
-    e = mxattn::launch_quant_hadamard(Q, eb, (int)d, B * H * Nq, qc, qs, rule, c, nullptr, s);
-    if (e == hipSuccess) e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ks, rule, c, nullptr, s);
-  } else {
-    e = mxattn::launch_quant_last(Q, eb, B * H * Nq * d / 32, qc, qs, rule, nullptr, s);
-    if (e == hipSuccess) e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, nullptr, s);
-  }
+  if (hadamard)
+    e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ks, rule, c, nullptr, s);
+  else
+    e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, nullptr, s);
   if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vs, rule, nullptr, s);
   if (e != hipSuccess) return hip_fail(e, who);
-  return attention_core(qc, qs, kc, ks, vc, vs, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O, dtype, nullptr,
-                        nullptr, s, who);
+  // Q is read once per query tile: the attention kernel rotates and quantises it itself
+  const QuantQ fused{Q, eb == 2, hadamard != 0, c};
+  return attention_core(nullptr, nullptr, kc, ks, vc, vs, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O, dtype,
+                        nullptr, nullptr, s, who, &fused);
 }
 
 }  // extern "C"

@@ -424,6 +424,81 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   }
 }
 
+// Fused Q quantisation (mxattn_forward): lane (r, g) turns elements 32g .. 32g + 31 of
+// query row `row` into one MXFP4 block exactly as the standalone quantiser does -- the
+// fp32 butterflies h = 1, 2, ..., d/2 (pairs (i, i + h) -> (a + b, a - b)), one multiply
+// by fl32(1/sqrt d), the block max, the shared exponent and the rounding conversion --
+// so the codes are bit-identical to mxattn_quantize's.  Butterflies h = 1..16 run in the
+// lane; h = 32 and h = 64 pair the lanes holding blocks g ^ 1 and g ^ 2 (16 and 32 lanes
+// apart).  Every lane of the wave takes part in the exchanges; lanes with g >= d/32 hold
+// zeros and produce code 0 with scale 127.
+template <int D>
+__device__ __forceinline__ void quantise_q_block(const AttnArgs& a, int64_t row, int g, Rule rule,
+                                                 uint32_t (&w)[4], int& sc) {
+  constexpr int GK = D / 32;
+  float v[32];
+  if (g < GK) {
+    if (a.q_bf16) {
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.qraw) + row * D + 32 * g);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 u = src[k];
+        v[8 * k + 0] = bf16lo(u.x); v[8 * k + 1] = bf16hi(u.x);
+        v[8 * k + 2] = bf16lo(u.y); v[8 * k + 3] = bf16hi(u.y);
+        v[8 * k + 4] = bf16lo(u.z); v[8 * k + 5] = bf16hi(u.z);
+        v[8 * k + 6] = bf16lo(u.w); v[8 * k + 7] = bf16hi(u.w);
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.qraw) + row * D + 32 * g);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float4 u = src[k];
+        v[4 * k + 0] = u.x; v[4 * k + 1] = u.y; v[4 * k + 2] = u.z; v[4 * k + 3] = u.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  if (a.q_hadamard) {
+#pragma unroll
+    for (int h = 1; h < 32; h *= 2) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        if ((i & h) == 0) {
+          const float x = v[i], y = v[i + h];
+          v[i] = x + y;
+          v[i + h] = x - y;
+        }
+      }
+    }
+#pragma unroll
+    for (int st = 1; st < GK; st *= 2) {  // h = 32 st: the partner holds block g ^ st
+      const uint32_t sgn = (uint32_t)(g & st) != 0 ? 0x80000000u : 0u;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float p = __shfl_xor(v[i], 16 * st);
+        v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ sgn);  // a + b, or b-lane: a + (-b)
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = v[i] * a.q_c;
+  }
+  if (g >= GK) return;
+  // integer max of |bits| (this file is built assuming no NaNs, so no float max here):
+  // NaN and Inf sort above every finite value
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+  if (mb >= 0x7F800000u) {
+    sc = 0xFF;  // a non-finite block: codes 0, scale NaN, as the quantiser writes it
+    return;
+  }
+  const int e = mx_exponent(mb, rule);
+  quant32(v, e, w);
+  sc = e + 127;
+}
+
 // One workgroup = NW waves; wave w owns QG groups of 16 queries.
 template <int D, int QG, bool PNQ, bool DUMP>
 __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
@@ -464,7 +539,9 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
                     a.vc + head * (int64_t)D * (kvp / 2), a.vs + head * (int64_t)D * (kvp / 32),
                     nkv * (D / 2), nkv * (D / 32), D * (kvp / 2), D * (kvp / 32)};
 
-  // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop
+  // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop: lane (r, g) holds
+  // block g of query row r.  Either read from the quantised Q^, or made here from the
+  // raw query rows (the fused prologue of mxattn_forward), see quantise_q_block.
   v8i qf[QG];
   int qsc[QG];
   int64_t qrow[QG];
@@ -473,13 +550,16 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
     int64_t q = (int64_t)qt * BR + wave * (16 * QG) + qg * 16 + r;
     qrow[qg] = q;
     const int64_t qq = q < a.nq ? q : a.nq - 1;
-    uint4 w = make_uint4(0, 0, 0, 0);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
     int sc = 127;
-    if (g < G::GK) {
-      w = *reinterpret_cast<const uint4*>(qc + qq * (D / 2) + 16 * g);
+    if (a.qraw) {
+      quantise_q_block<D>(a, head * a.nq + qq, g, prule, w, sc);
+    } else if (g < G::GK) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qc + qq * (D / 2) + 16 * g);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
       sc = qs[qq * (D / 32) + g];
     }
-    qf[qg] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    qf[qg] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
     qsc[qg] = sc;
   }
 

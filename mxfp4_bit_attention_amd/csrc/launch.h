@@ -44,6 +44,12 @@ struct AttnArgs {
   int64_t kv_pad;  // P: padded tokens of the transposed V layout
   float scale_log2;  // softmax_scale * log2(e)
   int out_bf16;
+  // Unquantised Q [heads, nq, d] (bf16 or fp32): when set, the kernel rotates and
+  // quantises its own query rows in its prologue (with the P~ rule) and qc/qs are unused.
+  const void* qraw;
+  int q_bf16;
+  int q_hadamard;
+  float q_c;  // fl32(1/sqrt(d)), the rotation's final multiplier
 };
 
 hipError_t launch_attention(const AttnArgs& a, int d, int pnq, Rule p_rule, hipStream_t s);

@@ -195,3 +195,34 @@ def test_repeatable_bitwise():
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+
+
+@pytest.mark.parametrize("dtype,d,had,rule", [("bf16", 128, True, "uos"), ("bf16", 128, False, "ocp"),
+                                              ("f32", 64, True, "tfs"), ("f32", 128, True, "q7.5")])
+def test_fused_q_quantisation_is_bitwise_the_quantiser(dtype, d, had, rule):
+    """mxattn_forward rotates and quantises Q inside the attention kernel: its output is
+    bitwise the output of mxattn_quantize(Q) followed by mxattn_forward_quantized on the
+    same K^ and V^ (a row holding NaN and Inf included)."""
+    torch, mx = require_gpu()
+    rng = np.random.default_rng(d + (7 if had else 0))
+    B, H, Nq, Nkv = 1, 3, 300, 517
+    Q = (rng.standard_normal((B, H, Nq, d)) * 2).astype(np.float32)
+    K = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    Q[0, 1, 7, 3] = np.nan
+    Q[0, 2, 11, 100 % d] = np.inf
+    if dtype == "bf16":
+        Q, K, V = (synth.bf16_to_f32(synth.round_to_bf16(a)) for a in (Q, K, V))
+    q, k, v = (to_device(a, dtype) for a in (Q, K, V))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    r = RULES[rule][0]
+    O = mx.mxattn_forward(q, k, v, scale, hadamard=had, pnq=True, rule=r)
+    qc, qs = mx.mxattn_quantize(q.view(-1, Nq, d), rule=r, axis="last", hadamard=had)
+    kc, ks = mx.mxattn_quantize(k.view(-1, Nkv, d), rule=r, axis="last", hadamard=had)
+    vc, vs = mx.mxattn_quantize(v.view(-1, Nkv, d), rule=r, axis="rows")
+    sh = lambda t: t.view(B, H, *t.shape[1:])
+    O2 = mx.mxattn_forward_quantized(sh(qc), sh(qs), sh(kc), sh(ks), sh(vc), sh(vs), Nkv, scale, pnq=True,
+                                     p_rule=r, out_dtype=O.dtype)
+    torch.cuda.synchronize()
+    iv = torch.int16 if O.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(O.view(iv), O2.view(iv))
