@@ -92,6 +92,11 @@ struct HadGeo {
     else if constexpr (D == 64 && EB == 2) return (r >> 1) & 7;  // 8 units/row, 2 rows per 256 B
     else return r & 15;                                        // fp32: 32 or 16 units/row
   }
+  // rows after which swz repeats, and the number of 1 KB DMAs that spans: DMA u of a
+  // chunk then reads at lane offset doff[u % PER] + 1024 (u - u % PER)
+  static constexpr int SWP = (D == 128 && EB == 2) ? 8 : 16;
+  static constexpr int PER = SWP * RB / 1024;
+  static_assert(NDMA % PER == 0, "DMA offset period");
 };
 
 template <int D, int EB, bool ERR>
@@ -109,10 +114,12 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
   int64_t chunk = (int64_t)blockIdx.x * G::NW + wave;
   const int64_t total = nrows * G::RB;
 
-  // per-lane DMA source offsets within a chunk (the same for every chunk)
-  uint32_t doff[G::NDMA];
+  // per-lane DMA source offsets within a chunk (the same for every chunk); the swizzle
+  // repeats every PER DMAs, so only PER of them are kept and the rest of the offset
+  // goes into the scalar offset of the transfer
+  uint32_t doff[G::PER];
 #pragma unroll
-  for (int u = 0; u < G::NDMA; ++u) {
+  for (int u = 0; u < G::PER; ++u) {
     const int slot = 64 * u + lane;  // 16-byte unit of the LDS chunk
     const int r = slot / G::CH, pos = slot % G::CH;
     doff[u] = (uint32_t)(r * G::RB + 16 * (pos ^ G::swz(r)));
@@ -125,7 +132,7 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
                                           0x00020000);
 #pragma unroll
     for (int u = 0; u < G::NDMA; ++u)
-      dma16(rs, buf + 1024 * u, doff[u]);
+      dma16_stream(rs, buf + 1024 * u, doff[u % G::PER], 1024 * (u - u % G::PER));
   };
 
   const int lr = lane / LPR;    // row within the chunk
@@ -314,7 +321,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
       const int slot = 64 * (NDMA * wave + u) + lane;  // 16-byte unit of the LDS tile
       const int r = slot / CH, pos = slot % CH;
       const int q = pos ^ (r >> 5);  // the global unit stored at `pos`
-      dma16(rs, tile + 1024 * (NDMA * wave + u), (uint32_t)(r * cols * EB + 16 * q));
+      dma16_stream(rs, tile + 1024 * (NDMA * wave + u), (uint32_t)(r * cols * EB + 16 * q), 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMAs have landed
@@ -382,10 +389,12 @@ hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, ui
                                  uint8_t* scales, Rule rule, float c, double* err, hipStream_t s) {
   const int rows_per_chunk = 64 / (d / 64);
   const int64_t nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
-  // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (three
-  // per CU for bf16 input, two for fp32, by registers and LDS), each looping over chunks
+  // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (four
+  // per CU for bf16 input, by registers (at most 128 VGPRs) and LDS (32 KB each); three
+  // for the error sums, which need a few more registers; two for fp32), each looping
+  // over chunks
   int64_t grid = (nchunks + 3) / 4;
-  const int64_t resident = 256 * (eb == 2 ? 3 : 2);
+  const int64_t resident = 256 * (eb == 2 ? (err ? 3 : 4) : 2);
   if (grid > resident) grid = resident;
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   const unsigned g = (unsigned)grid;
