@@ -86,11 +86,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
 }
-// Streaming forms for data read exactly once (the quantisers' inputs): a wave-uniform
-// offset `soff` goes into the scalar offset field, and the load is marked non-temporal
-// (cache-policy bit nt), which keeps it from displacing reused lines in the caches.
-__device__ __forceinline__ void dma16_stream(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, soff, 0, 2);
+// Streaming form for data read exactly once (the quantisers' inputs): the load is marked
+// non-temporal (cache-policy bit nt), which keeps it from displacing reused lines.
+__device__ __forceinline__ void dma16_stream(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 2);
 }
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);

@@ -92,11 +92,6 @@ struct HadGeo {
     else if constexpr (D == 64 && EB == 2) return (r >> 1) & 7;  // 8 units/row, 2 rows per 256 B
     else return r & 15;                                        // fp32: 32 or 16 units/row
   }
-  // rows after which swz repeats, and the number of 1 KB DMAs that spans: DMA u of a
-  // chunk then reads at lane offset doff[u % PER] + 1024 (u - u % PER)
-  static constexpr int SWP = (D == 128 && EB == 2) ? 8 : 16;
-  static constexpr int PER = SWP * RB / 1024;
-  static_assert(NDMA % PER == 0, "DMA offset period");
 };
 
 template <int D, int EB, bool ERR>
@@ -114,12 +109,10 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
   int64_t chunk = (int64_t)blockIdx.x * G::NW + wave;
   const int64_t total = nrows * G::RB;
 
-  // per-lane DMA source offsets within a chunk (the same for every chunk); the swizzle
-  // repeats every PER DMAs, so only PER of them are kept and the rest of the offset
-  // goes into the scalar offset of the transfer
-  uint32_t doff[G::PER];
+  // per-lane DMA source offsets within a chunk (the same for every chunk)
+  uint32_t doff[G::NDMA];
 #pragma unroll
-  for (int u = 0; u < G::PER; ++u) {
+  for (int u = 0; u < G::NDMA; ++u) {
     const int slot = 64 * u + lane;  // 16-byte unit of the LDS chunk
     const int r = slot / G::CH, pos = slot % G::CH;
     doff[u] = (uint32_t)(r * G::RB + 16 * (pos ^ G::swz(r)));
@@ -128,11 +121,12 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
     const int64_t left = total - ch * G::CB;
     const int n = left <= 0 ? 0 : (left > 0x7FFFFFFF ? 0x7FFFFFFF : (int)left);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(x + (ch < nchunks ? ch : 0) * G::CB), (short)0, n,
-                                          0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(x + ch * G::CB), (short)0, n, 0x00020000);
+    // the lane offsets are checked against the descriptor's size: rows past the end
+    // read as zero without a memory access.  The input is read once: non-temporal.
 #pragma unroll
     for (int u = 0; u < G::NDMA; ++u)
-      dma16_stream(rs, buf + 1024 * u, doff[u % G::PER], 1024 * (u - u % G::PER));
+      dma16_stream(rs, buf + 1024 * u, doff[u]);
   };
 
   const int lr = lane / LPR;    // row within the chunk
@@ -321,7 +315,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
       const int slot = 64 * (NDMA * wave + u) + lane;  // 16-byte unit of the LDS tile
       const int r = slot / CH, pos = slot % CH;
       const int q = pos ^ (r >> 5);  // the global unit stored at `pos`
-      dma16_stream(rs, tile + 1024 * (NDMA * wave + u), (uint32_t)(r * cols * EB + 16 * q), 0);
+      dma16_stream(rs, tile + 1024 * (NDMA * wave + u), (uint32_t)(r * cols * EB + 16 * q));
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's DMAs have landed
@@ -389,12 +383,10 @@ hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, ui
                                  uint8_t* scales, Rule rule, float c, double* err, hipStream_t s) {
   const int rows_per_chunk = 64 / (d / 64);
   const int64_t nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
-  // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (four
-  // per CU for bf16 input, by registers (at most 128 VGPRs) and LDS (32 KB each); three
-  // for the error sums, which need a few more registers; two for fp32), each looping
-  // over chunks
+  // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (three
+  // per CU for bf16 input, two for fp32, by registers and LDS), each looping over chunks
   int64_t grid = (nchunks + 3) / 4;
-  const int64_t resident = 256 * (eb == 2 ? (err ? 3 : 4) : 2);
+  const int64_t resident = 256 * (eb == 2 ? 3 : 2);
   if (grid > resident) grid = resident;
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   const unsigned g = (unsigned)grid;
