@@ -12,7 +12,11 @@ those sweeps on any tensor with the library's own kernels:
                                 attention when only the P~ tiles' rule varies;
   rowsum_decomposition(...)     how quantising P~ moves each row's normaliser, split
                                 into zeroed, saturated, rounded-down and rounded-up
-                                elements (from the kernel's P^ dump).
+                                elements (from the kernel's P^ dump);
+  global_scaling(...)           the post-normalisation arm with one global factor g
+                                applied to P before quantisation: the row sums of the
+                                quantised tile for each g, and the g that brings their
+                                average closest to one (Figure 7, panel C).
 
 Quantisation and attention run in libmxattn; torch only reduces the results.
 """
@@ -143,11 +147,56 @@ def rowsum_decomposition(q, k, v, softmax_scale: float, p_rule="uos", rule="uos"
             "total": float(((diff).sum(dim=1) / lt).mean()), "rows": int(rows.numel())}
 
 
+GAMMAS = tuple(1.0 + i / 512 for i in range(256))  # 1.000, 1.002, ..., 1.498
+
+
+def probabilities(q, k, v, softmax_scale: float, rows=None, rule="uos", hadamard: bool = True):
+    """One head.  P = softmax(S) in fp32 for the given query rows, with S from the
+    dequantised Q^ and K^ that the library's quantiser makes (the post-normalisation
+    arm materialises P; this is that P).  Returns P [rows, Nkv] on the GPU."""
+    import torch
+    n = q.shape[0]
+    rows = torch.arange(n, device=q.device) if rows is None else torch.as_tensor(rows, device=q.device)
+    qc, qsc, kc, ksc, _, _ = _quantized_head(q, k, v, rule, hadamard)
+    qd = _dequant_last(qc[rows], qsc[rows])
+    kd = _dequant_last(kc, ksc)
+    return torch.softmax((qd @ kd.t().contiguous()) * softmax_scale, dim=-1).contiguous()
+
+
+def global_scaling_rowsums(P, p_rule="uos", gammas=GAMMAS):
+    """P [rows, n] fp32 on the GPU.  For each g: y = g * P (fp32), block-quantised along
+    each row by the library's quantiser, dequantised and summed per row in float64 (the
+    factor stays in the weights: it compensates the average loss of quantisation).
+    Returns a float64 tensor [len(gammas), rows]."""
+    import torch
+    rows, n = P.shape
+    pad = -(-n // 32) * 32
+    y = torch.zeros((rows, pad), dtype=torch.float32, device=P.device)
+    out = torch.empty((len(gammas), rows), dtype=torch.float64, device=P.device)
+    for i, g in enumerate(gammas):
+        y[:, :n] = P * float(np.float32(g))
+        c, s = mxattn_quantize(y, rule=p_rule, axis="last")
+        out[i] = _dequant_last(c, s).double().sum(dim=1)
+    return out
+
+
+def global_scaling(P, p_rule="uos", gammas=GAMMAS):
+    """Summary of global_scaling_rowsums: the g whose mean row sum is closest to one, and
+    the mean, standard deviation and largest |row sum - 1| at g = 1 and at that g."""
+    rs = global_scaling_rowsums(P, p_rule, gammas)
+    mean = rs.mean(dim=1)
+    best = int((mean - 1.0).abs().argmin())
+    stats = lambda r: {"mean": float(r.mean()), "std": float(r.std()), "max_abs_dev": float((r - 1).abs().max())}
+    return {"g_best": gammas[best], "at_g1": stats(rs[0]), "at_g_best": stats(rs[best]),
+            "mean_curve": [round(float(x), 6) for x in mean]}
+
+
 def main() -> None:
-    """The three diagnostics on the Wan2.2-720p-shaped synthetic tensors (one JSON line):
-    the Qmax sweep of Q and K (rotated, along d) and V (along tokens) over all 40 heads,
-    the P~-tile sweep on head 0 (1024 sampled query rows against exact attention), and
-    the row-sum decomposition on the first 8192 tokens of head 0 (512 rows)."""
+    """The diagnostics on the Wan2.2-720p-shaped synthetic tensors (one JSON line): the
+    Qmax sweep of Q and K (rotated, along d) and V (along tokens) over all 40 heads, the
+    P~-tile sweep on head 0 (1024 sampled query rows against exact attention), the row-sum
+    decomposition on the first 8192 tokens of head 0 (512 rows), and the global-scaling arm
+    on 256 rows of head 0's materialised P (all 75,600 keys)."""
     import json
     import os
     import sys
@@ -175,6 +224,9 @@ def main() -> None:
     res["rowsum_decomposition"] = {
         r: rowsum_decomposition(sub(q), sub(k), sub(v), float(w.softmax_scale), p_rule=r, rule=r, rows=rrows)
         for r in ("uos", "ocp")}
+    P = probabilities(q[0], k[0], v[0], float(w.softmax_scale), rows=torch.linspace(0, w.N - 1, 256, device=dev).long())
+    res["global_scaling"] = {"rows": 256, **{r: global_scaling(P, p_rule=r) for r in ("uos", "ocp")}}
+    del P
     print(json.dumps(res), flush=True)
 
 

@@ -8,6 +8,12 @@ rowsum_decomposition  replays the PNQ online softmax of one head (the tile recur
                       zeroed (code 0 for P~ > 0), saturated (P~ / 2^e >= 7: round-to-
                       nearest heads for 8 and the format clips to 6), rounded down,
                       rounded up; each as a mean fraction of l~ = sum P~ over the rows.
+global_scaling_rowsums  the post-normalisation arm with pre-quantisation global scaling:
+                      the materialised probabilities P (fp32) are multiplied by one scalar
+                      g and quantised in 32-key blocks; returns the row sums of the
+                      dequantised tile for each g (Pith review, Figure 7 caption, panel C:
+                      such a global factor can bring the *average* row sum back to one,
+                      which leaves each row's own error in place).
 
 The question they answer is the one the Pith review's referee report raises: the UOS
 constant is derived for a model density of block maxima, and per-block Qmax sweeps on
@@ -86,4 +92,19 @@ def rowsum_decomposition(Qc, Qs, Kc, Ks, Nkv: int, softmax_scale: float, p_rule,
         m = m_new
     out = {c: float((acc[c] / lt).mean()) for c in classes}
     out["total"] = float((sum(acc[c] for c in classes) / lt).mean())
+    return out
+
+
+def global_scaling_rowsums(P, p_rule, gammas):
+    """P [rows, n] fp32 probabilities (each row a softmax).  For every g in gammas:
+    y = fl32(g * P) (one IEEE fp32 multiply), quantised in 32-key blocks along each row
+    under p_rule and dequantised (exact in float64).  Returns the float64 row sums
+    [len(gammas), rows] of the dequantised y: the factor is a compensation that stays in
+    the weights, chosen to pull the average row sum of the quantised tile back to one."""
+    P = np.asarray(P, dtype=np.float32)
+    out = np.empty((len(gammas), P.shape[0]), dtype=np.float64)
+    for i, g in enumerate(gammas):
+        y = (np.float32(g) * P).astype(np.float32)
+        codes, scales = mxfp4.quantize_blocks_lastaxis(y, p_rule)
+        out[i] = mxfp4.dequantize_blocks_lastaxis(codes, scales)[:, : P.shape[1]].sum(axis=1)
     return out

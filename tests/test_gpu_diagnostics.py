@@ -109,3 +109,25 @@ def test_rowsum_decomposition_matches_oracle(rule):
     o = od.rowsum_decomposition(Qc, Qs, Kc, Ks, n, scale, RULES[rule][1], mx.mxattn_kv_tile())
     for c in ("zeroed", "saturated", "rounded_down", "rounded_up", "total"):
         assert abs(g[c] - o[c]) < 1e-4 + 1e-3 * abs(o[c]), (c, g[c], o[c])
+
+
+@pytest.mark.parametrize("rule", ["uos", "ocp"])
+def test_global_scaling_matches_oracle(rule):
+    """The global-scaling arm: the GPU's row sums of the quantised g * P equal the
+    oracle's on the same fp32 P (the quantiser is bit-exact; only the float64 summation
+    order differs), for a few g and for the g the sweep picks."""
+    torch, mx = require_gpu()
+    from mxfp4_bit_attention_amd import diagnostics as dg
+    w = synth.TINY
+    Q, K, V = (synth.attn_tensor(w, t) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
+    q, k, v = (to_device(x[0, 0], "f32") for x in (Q, K, V))
+    P = dg.probabilities(q, k, v, float(np.float32(w.softmax_scale)), rule=RULES[rule][0])
+    gs = (1.0, 1.03, 1.0625, 1.3, 2.0)
+    g_rs = dg.global_scaling_rowsums(P, p_rule=RULES[rule][0], gammas=gs).cpu().numpy()
+    o_rs = od.global_scaling_rowsums(P.cpu().numpy(), RULES[rule][1], gs)
+    np.testing.assert_allclose(g_rs, o_rs, rtol=1e-12, atol=0)
+    summary = dg.global_scaling(P, p_rule=RULES[rule][0])
+    o_all = od.global_scaling_rowsums(P.cpu().numpy(), RULES[rule][1], dg.GAMMAS)
+    best = int(np.abs(o_all.mean(axis=1) - 1).argmin())
+    assert summary["g_best"] == dg.GAMMAS[best]
+    assert summary["at_g1"]["mean"] == pytest.approx(o_all[0].mean(), rel=1e-12)

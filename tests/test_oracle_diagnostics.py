@@ -92,3 +92,62 @@ def test_rowsum_direct_placement_drifts_down():
     Kc, Ks = ora.quantize_qk(K, mxfp4.UOS, True)
     dec = od.rowsum_decomposition(Qc, Qs, Kc, Ks, 512, scale, mxfp4.UOS, 128)
     assert dec["total"] < 0 and dec["zeroed"] < 0
+
+
+# ---- global-scaling arm (post-normalisation P, one factor g before quantisation)
+
+def test_global_scaling_one_hot_rows_closed_form():
+    """A one-hot row holds the single value g, whose block max is g.  Under UOS
+    (smallest e with g <= 7.25 * 2^e) the scaled value g / 2^e rounds to a grid point G,
+    and the row sum is G * 2^e.  Worked by hand:
+      g = 1   : e = -2, 4.0 -> 4 : 1
+      g = 1.1 : e = -2, 4.4 -> 4 : 1
+      g = 1.3 : e = -2, 5.2 -> 6 : 1.5
+      g = 1.9 : e = -1, 3.8 -> 4 : 2"""
+    P = np.zeros((3, 96), np.float32)
+    P[0, 0] = P[1, 40] = P[2, 95] = 1.0
+    rs = od.global_scaling_rowsums(P, mxfp4.UOS, [1.0, 1.1, 1.3, 1.9])
+    for i, w in enumerate([1.0, 1.0, 1.5, 2.0]):
+        assert np.all(rs[i] == w), (i, rs[i], w)
+
+
+def test_global_scaling_power_of_two_factor_scales_the_sums():
+    """A power-of-two g moves every block scale by the same power: the row sums scale
+    by g exactly."""
+    rng = np.random.default_rng(7)
+    S = rng.standard_normal((16, 200)) * 3
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P = (P / P.sum(axis=1, keepdims=True)).astype(np.float32)
+    for rule in (mxfp4.UOS, mxfp4.OCP):
+        rs = od.global_scaling_rowsums(P, rule, [1.0, 2.0, 0.25, 1024.0])
+        for i, g in enumerate([1.0, 2.0, 0.25, 1024.0]):
+            assert np.array_equal(rs[i], rs[0] * g)
+
+
+def test_global_scaling_grid_rows_and_ties():
+    """[1/2, 1/4, 1/8, 1/8]: block max 1/2, UOS e = -3 (1/2 <= 7.25/8), scaled values
+    4, 2, 1, 1 -- grid points -- so the row sum is exactly 1 at g = 1.  At g = 1.25 the
+    block max is 0.625, e = -3 again, scaled values 5, 2.5, 1.25, 1.25 are all ties that
+    go to the even code: 4, 2, 1, 1, so the sum is (4 + 2 + 1 + 1) / 8 = 1 although the
+    weights were scaled up by 1.25.  At g = 1.5: 6, 3, 1.5, 1.5, all on the grid: 1.5."""
+    P = np.zeros((1, 32), np.float32)
+    P[0, :4] = [0.5, 0.25, 0.125, 0.125]
+    rs = od.global_scaling_rowsums(P, mxfp4.UOS, [1.0, 1.25, 1.5])
+    assert rs[0, 0] == 1.0 and rs[1, 0] == 1.0 and rs[2, 0] == 1.5
+
+
+def test_global_scaling_moves_the_mean_not_the_rows():
+    """On softmax rows of Gaussian logits the quantised rows sum to less than one on
+    average; a factor g a little above one brings the average back to one, and the rows'
+    spread around their mean stays of the same size."""
+    rng = np.random.default_rng(11)
+    S = rng.standard_normal((64, 512)) * 2.5
+    P = np.exp(S - S.max(axis=1, keepdims=True))
+    P = (P / P.sum(axis=1, keepdims=True)).astype(np.float32)
+    gs = [1.0 + i / 256 for i in range(64)]
+    rs = od.global_scaling_rowsums(P, mxfp4.UOS, gs)
+    mean = rs.mean(axis=1)
+    assert mean[0] < 0.97 and mean.max() > 1.0
+    best = int(np.abs(mean - 1).argmin())
+    assert abs(mean[best] - 1) < 0.005
+    assert rs[best].std() > 0.5 * rs[0].std()
