@@ -151,7 +151,8 @@ ABLATION_RULES = (("uos", "uos"), ("ocp", "ocp"), ("tfs_q6", ("ceil", 6.0)), ("o
 def extras(torch, mx, w, q, k, v, out, ws, stream, iters: int = 5) -> dict:
     """Scale-rule ablation of the full step at the headline shape (the same rule for
     Q, K, V and the P~ tiles), and the step at other shapes the boundary takes: d = 64,
-    two batch entries, and a short key sequence (text-like cross-attention)."""
+    two batch entries, a short key sequence (text-like cross-attention), and the
+    Wan2.2-480p and HunyuanVideo-720p workloads."""
     res = {}
     ab = {}
     for name, rule in ABLATION_RULES:
@@ -179,6 +180,19 @@ def extras(torch, mx, w, q, k, v, out, ws, stream, iters: int = 5) -> dict:
         ms = time_launches(torch, fn, iters, stream)
         flops = 4.0 * sh["B"] * sh["H"] * sh["Nq"] * sh["Nkv"] * sh["d"]
         shapes[name] = dict(sh, ms_per_step=round(ms, 3), TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1))
+        del qq, kk, vv, oo, wws
+    # the pages' other two workloads, full step on their synthetic tensors
+    for wl in (synth.WAN_480P, synth.HUNYUAN_720P):
+        qq, kk, vv = (synth.device_attn_tensor(wl, t, q.device) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
+        oo = torch.empty_like(qq)
+        wws = torch.empty(mx.mxattn_forward_workspace_bytes(wl.B, wl.H, wl.N, wl.N, wl.d), dtype=torch.uint8,
+                          device=q.device)
+        fn = lambda: mx.mxattn_forward(qq, kk, vv, float(wl.softmax_scale), hadamard=True, pnq=True, rule="uos",
+                                       out=oo, workspace=wws)
+        fn()
+        ms = time_launches(torch, fn, iters, stream)
+        shapes[wl.name] = dict(B=wl.B, H=wl.H, Nq=wl.N, Nkv=wl.N, d=wl.d, ms_per_step=round(ms, 3),
+                               TFLOPs=round(wl.flops / (ms * 1e-3) / 1e12, 1))
         del qq, kk, vv, oo, wws
     res["other_shapes"] = shapes
     return res
