@@ -87,7 +87,16 @@ def test_ablation_rules_p_codes(rule, Nq, Nkv, d):
     test_quantized_entry_p_codes(rule, Nq, Nkv, d)
 
 
-@pytest.mark.parametrize("B,H,Nq,Nkv,d,dtype", [(2, 2, 300, 700, 128, "bf16"), (3, 1, 129, 257, 64, "f32")])
+@pytest.mark.parametrize("rule", ["uos"])
+def test_long_kv_sequence_p_codes(rule):
+    """Five query rows against 150,001 keys (1,172 kv tiles, a ragged last one): every
+    output row and every P^ code against the oracle, so the running max and the rescale
+    are exercised over a sequence twice as long as the headline one."""
+    test_quantized_entry_p_codes(rule, 5, 150001, 128)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nkv,d,dtype", [(2, 2, 300, 700, 128, "bf16"), (3, 1, 129, 257, 64, "f32"),
+                                                (1, 1, 5, 150001, 128, "bf16")])
 def test_batched_cross_shape_pipeline(B, H, Nq, Nkv, d, dtype):
     """B > 1 and N_q != N_kv through mxattn_forward (Hadamard, UOS, PNQ); every row of
     every (batch, head) against the oracle pipeline."""
