@@ -18,7 +18,7 @@ Sources (page titles and sections):
     exponentials first and uses that one result for both the normaliser and
     the output update.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * Blocks run along the contraction axis: d for Q and K, tokens for V, kv
     for P~ (aligned to kv index 0).  Ragged tails are zero-padded; padded
     keys get P~ = 0.

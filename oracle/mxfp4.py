@@ -19,7 +19,7 @@ Sources (the pages' titles and sections):
   * Appendix A opening (Pith review, end of the reference list): the all-zero
     block and out-of-range exponents are left to the MXFP4 conversion routine.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * Grid {0, .5, 1, 1.5, 2, 3, 4, 6}; code = sign << 3 | magnitude index
     (the OCP E2M1 bit layout, where the index is the magnitude's rank).
   * Rounding: nearest grid point; a tie goes to the even code.  Values above
