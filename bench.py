@@ -3,9 +3,9 @@
 
 One step = the whole hot path on the Wan2.2-720p-shaped self-attention
 (B=1, H=40, N_q=N_kv=75,600, d=128, bf16 inputs resident in HBM): Hadamard +
-UOS quantisation of Q and K along d, UOS quantisation of V along tokens, and
-the fused MXFP4 flash attention with PNQ.  Throughput is 4 B H N_q N_kv d per
-step time, in TFLOP/s.
+UOS quantisation of K along d, UOS quantisation of V along tokens, and the fused
+MXFP4 flash attention with PNQ, which rotates and quantises Q itself as it loads
+its query rows.  Throughput is 4 B H N_q N_kv d per step time, in TFLOP/s.
 
 Printed as one JSON line, with:
   roofline       the attention kernel (dominant) against the dense MXFP4 MFMA
@@ -16,8 +16,9 @@ Printed as one JSON line, with:
                  bf16 against HBM bandwidth (UOS, OCP and q = 6);
   rule_ablation  the full step under each shared-exponent rule (UOS, OCP, TFS,
                  OAS and CEIL 7.5; the same rule for Q, K, V and P~);
-  other_shapes   the full step at d = 64, at B = 2 x H = 20, and with 512 keys
-                 (cross-attention-like);
+  other_shapes   the full step at d = 64, at B = 2 x H = 20, with 512 keys
+                 (cross-attention-like), and on the Wan2.2-480p and
+                 HunyuanVideo-720p workloads;
   cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
                  on this host, extrapolated to the full workload.
 
