@@ -178,7 +178,8 @@ int quantize_impl(const void* x, int32_t dtype, int64_t batch, int64_t rows, int
     return fail(MXATTN_E_INVALID, "%s: axis must be MXATTN_AXIS_LAST or MXATTN_AXIS_ROWS", who);
   }
   hipError_t e = hipSuccess;
-  if (err) e = hipMemsetAsync(err, 0, 3 * sizeof(double), s);
+  // a kernel rather than a memset clears the sums, so the call can be captured in a graph
+  if (err) e = mxattn::launch_zero_f64(err, 3, s);
   if (e == hipSuccess) {
     if (axis == MXATTN_AXIS_LAST && hadamard)
       e = mxattn::launch_quant_hadamard(x, eb, (int)cols, batch * rows, codes, scales, rule, inv_sqrt_f32((int)cols),

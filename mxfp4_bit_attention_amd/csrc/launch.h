@@ -27,6 +27,8 @@ hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* co
 // Quantise down the rows, transposed output with P (multiple of 128) padded tokens.
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
                              int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s);
+// Sets n doubles to zero with a kernel (graph-capturable, unlike a memset node).
+hipError_t launch_zero_f64(double* p, int n, hipStream_t s);
 
 struct AttnArgs {
   const uint8_t* qc;

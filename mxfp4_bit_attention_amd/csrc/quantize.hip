@@ -369,6 +369,11 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
   if constexpr (ERR) acc.flush(err);
 }
 
+__global__ void k_zero_f64(double* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0;
+}
+
 // ---------------------------------------------------------------------------
 // Launchers.  With err == nullptr the kernels store codes and scales; otherwise they
 // store nothing and add the quantisation error sums to err[0..2] (the Qmax sweep).
@@ -401,6 +406,11 @@ hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, ui
                                  : launch_h<64, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_f64(double* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_f64, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, s, p, n);
   return hipGetLastError();
 }
 
