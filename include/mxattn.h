@@ -16,7 +16,8 @@
  *    buffer (inputs, outputs, workspace).  The library never allocates, frees
  *    or synchronises device memory.  Work is enqueued on `stream` (a
  *    hipStream_t; NULL = the null stream) and the call returns without
- *    waiting.
+ *    waiting.  Every call enqueues kernels only (no memset or copy nodes), so it
+ *    can be captured into a HIP graph and replayed.
  *  - Tensors are dense, row-major (last index fastest), 16-byte aligned.
  *  - Arguments are checked on the host before any HIP call.  A failed check
  *    returns a negative mxattn_status and sets a thread-local message
@@ -117,7 +118,7 @@ int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, i
  *   sums[2] = number of blocks left out because they hold Inf or NaN,
  * where "value" is what was quantised (the rotated fp32 value with hadamard != 0).
  * sums: 3 doubles of device memory, 8-byte aligned, owned by the caller; the call
- * zeroes them on `stream` before adding.  Per-block sums are fp32, the totals fp64.
+ * zeroes them on `stream` (with a kernel) before adding.  Per-block sums are fp32, the totals fp64.
  */
 int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols,
                        int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
