@@ -118,7 +118,8 @@ int mxattn_quantize(const void* x, int32_t dtype, int64_t batch, int64_t rows, i
  *   sums[2] = number of blocks left out because they hold Inf or NaN,
  * where "value" is what was quantised (the rotated fp32 value with hadamard != 0).
  * sums: 3 doubles of device memory, 8-byte aligned, owned by the caller; the call
- * zeroes them on `stream` (with a kernel) before adding.  Per-block sums are fp32, the totals fp64.
+ * zeroes them on `stream` (with a kernel) before adding.  Per-block sums are fp32,
+ * the totals fp64.
  */
 int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows, int64_t cols,
                        int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
