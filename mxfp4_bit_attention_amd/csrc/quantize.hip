@@ -285,11 +285,14 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
 // so that the column reads below spread over all banks.  Thread t then quantises
 // columns 2p, 2p + 1 (p = t / 8) over the 32 tokens of block t % 8: the eight lanes
 // of a column pair write the column's 128 code bytes of the tile contiguously.
-// blockIdx.x: token tile; blockIdx.y: column tile; blockIdx.z: batch.
+// Tiles are numbered token tile fastest, then column tile, then batch item, and dealt
+// to the eight XCDs in contiguous ranges (workgroups go to the XCDs round-robin): the
+// tiles that complete each other's partial 128-byte lines of codes and scales (a
+// channel's row is not a multiple of 128 bytes) then write through the same L2.
 
 template <int EB, bool ERR>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t P,
+                                                    int64_t cols, int64_t P, int64_t batch,
                                                     uint8_t* __restrict__ codes,
                                                     uint8_t* __restrict__ scales, Rule rule, double* err) {
   constexpr int TT = 256;         // tokens per tile
@@ -301,9 +304,13 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t t0 = (int64_t)blockIdx.x * TT;
-  const int64_t c0 = (int64_t)blockIdx.y * TC;
-  const int64_t b = blockIdx.z;
+  const int64_t nx = (P + TT - 1) / TT, ny = (cols + TC - 1) / TC;
+  const int64_t per_xcd = (int64_t)(gridDim.x / 8);
+  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (item >= nx * ny * batch) return;
+  const int64_t t0 = (item % nx) * TT;
+  const int64_t c0 = ((item / nx) % ny) * TC;
+  const int64_t b = item / (nx * ny);
   {
     // descriptor over this batch item from token t0, column c0 to its end
     const int64_t left = ((rows - t0) * cols - c0) * EB;
@@ -428,16 +435,22 @@ hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* co
 
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
                              int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s) {
-  dim3 grid((unsigned)((P + 255) / 256), (unsigned)((cols + 63) / 64), (unsigned)batch);
+  const int64_t tiles = (P + 255) / 256 * ((cols + 63) / 64) * batch;
+  if (tiles > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   if (eb == 2 && err)
-    hipLaunchKernelGGL((k_quant_rows<2, true>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
+    hipLaunchKernelGGL((k_quant_rows<2, true>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
+                       err);
   else if (eb == 2)
-    hipLaunchKernelGGL((k_quant_rows<2, false>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
+    hipLaunchKernelGGL((k_quant_rows<2, false>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
+                       err);
   else if (err)
-    hipLaunchKernelGGL((k_quant_rows<4, true>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
+    hipLaunchKernelGGL((k_quant_rows<4, true>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
+                       err);
   else
-    hipLaunchKernelGGL((k_quant_rows<4, false>), grid, dim3(256), 0, s, xp, rows, cols, P, codes, scales, rule, err);
+    hipLaunchKernelGGL((k_quant_rows<4, false>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
+                       err);
   return hipGetLastError();
 }
 
