@@ -276,7 +276,7 @@ def main():
     abytes = attn_algorithmic_bytes(w)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4), "traffic": read_traffic(abytes),
-                "kernel": "k_attn<128,2,PNQ>", "ms_per_launch": round(ms_attn, 3),
+                "kernel": "k_attn<128,PNQ>", "ms_per_launch": round(ms_attn, 3),
                 "algorithmic_bytes": abytes}
 
     result = {

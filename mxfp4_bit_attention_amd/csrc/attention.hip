@@ -7,19 +7,23 @@
 // normalised weights sum to one by construction.  With PNQ off the row sum
 // uses the unquantised P~ (the direct placement of Figure 4(C)).
 //
-// Both products are block-scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4 with
-// fp4 operands and E8M0 scales), computed transposed so that every lane owns
-// one query and one aligned 32-key block:
-//   S^T = K^ Q^^T  : A = 16 keys x 128 d (from LDS), B = Q^ (registers).
-//                    The 16 key rows of MFMA t are keys 32(r/4) + 4t + (r%4),
-//                    r = 0..15, so after the 8 MFMAs of a 128-key tile lane
-//                    l holds S(query l%16, keys 32(l/16) .. 32(l/16)+31).
-//   O^T += V^^T P^^T : A = 16 channels x 128 kv (from LDS), B = P^, which is
-//                    exactly the lane's 32 quantised values plus their E8M0
-//                    scale, so P^ never leaves registers.
-// The row max needs two cross-lane steps (v_permlane16_swap, v_permlane32_swap);
-// the PNQ row sum is one extra MFMA against an all-ones A operand, which sums
-// the same P^ codes the P^ V product uses.
+// Both products are block-scaled 32x32x64 MFMAs (v_mfma_scale_f32_32x32x64_f8f6f4
+// with fp4 operands and E8M0 scales), computed transposed so that every lane owns
+// one query and two aligned 32-key blocks of each 128-key tile.  Lane (i, h)
+// (i = lane % 32, h = lane / 32):
+//   S^T = K^ Q^^T  : MFMA (t, s), t = 0..3, s = 0..d/64-1: A = 32 keys x 64 d (LDS),
+//                    B = Q^ (registers, query i, d-block 2s + h).  Row rho of MFMA t
+//                    is key kappa(t, rho), chosen so that output element v of lane
+//                    (i, h) is key 64(t/2) + 32h + 16(t%2) + v of query i: after the
+//                    four MFMAs the lane holds keys 64c + 32h + 0..31 (c = 0, 1).
+//   O^T += V^^T P^^T : MFMA (ct, c): A = 32 channels x 64 keys (LDS), B = P^ of the
+//                    64-key chunk c, which is exactly the lane's block c quantised
+//                    in registers with its E8M0 byte, so P^ never leaves registers.
+// The row max needs one cross-lane step (v_permlane32_swap); the PNQ row sum is one
+// extra MFMA per chunk against an all-ones A operand, which sums the same P^ codes
+// the P^ V product uses.  A 32x32x64 MFMA leaves the vector ALU free for part of
+// its duration (the 16x16x128 form does not), so ALU work placed beside these
+// MFMAs, in this wave or in the other wave of the SIMD, runs in their shadow.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,28 +35,24 @@
 namespace mxattn {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in registers
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // D = A * B + C with fp4 A and B, E8M0 scales chosen by byte OPA of sa / byte 0 of sb.
 template <int OPA>
-__device__ __forceinline__ v4f mma(const v8i& a, const v8i& b, const v4f& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OPA, sa, 0, sb);
+__device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, OPA, sa, 0, sb);
 }
 
-__device__ __forceinline__ float xmax4(float x) {
-  // max over lanes l, l^16, l^32, l^48
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+// max / sum over lanes l and l ^ 32
+__device__ __forceinline__ float xmax2(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
-
-__device__ __forceinline__ float xsum4(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+__device__ __forceinline__ float xsum2(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -62,11 +62,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 constexpr int BC = kKvTile;  // 128 keys per kv tile
-// A workgroup is 4 waves (one per SIMD) and two workgroups share a CU: each SIMD
-// then runs one wave of each, and since the workgroups synchronise on separate
-// barriers they drift out of phase, so one wave's softmax overlaps the other's MFMAs.
+// A workgroup is 4 waves (one per SIMD) of 32 queries each, and two workgroups share
+// a CU: each SIMD then runs one wave of each, and since the workgroups synchronise on
+// separate barriers they drift out of phase, so one wave's softmax runs beside the
+// other's MFMAs.
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;  // threads per workgroup
+constexpr int BR = 32 * NW;  // queries per workgroup
 
 // s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding: vmcnt low
 // bits [3:0] and high bits [15:14], expcnt [6:4], lgkmcnt [11:8]).
@@ -75,14 +77,14 @@ constexpr int NT = 64 * NW;  // threads per workgroup
 // One kv tile in LDS.  Every region is filled by global->LDS DMA, where lane L of a
 // wave writes 16 (or 4) bytes at base + 16 L (or 4 L); the layouts below are chosen
 // so that each MFMA fragment is one contiguous 1 KB read per wave.
-//  K codes  [t][g][r] 16-byte units: unit (t, g, r) = d-block g of key kappa(t, r)
-//  K scales [8 r + t] dwords: the D/32 scale bytes of key kappa(t, r)
-//  V codes  [ct][g][r]: unit (ct, g, r) = keys 32 g .. 32 g + 31 of channel 16 ct + r
-//  V scales [NCT r + ct] dwords: the 4 scale bytes (one per 32-key block) of channel 16 ct + r
+//  K codes  [t][s][l] 16-byte units: unit (t, s, l) = d-block 2s + l/32 of key kappa(t, l%32)
+//  K scales [4 i + t] dwords: the d/32 scale bytes of key kappa(t, i)
+//  V codes  [ct][c][l]: unit (ct, c, l) = keys 64c + 32(l/32) .. +31 of channel 32ct + l%32
+//  V scales [NCT i + ct] dwords: the 4 scale bytes (one per 32-key block) of channel 32ct + i
 template <int D>
 struct Geo {
-  static constexpr int NCT = D / 16;        // 16-channel tiles of O
-  static constexpr int GK = D / 32;         // 32-element blocks per key row
+  static constexpr int S = D / 64;     // d-steps of an S^T MFMA
+  static constexpr int NCT = D / 32;   // 32-channel tiles of O
   static constexpr int KC = BC * D / 2;
   static constexpr int KS = 4 * BC;
   static constexpr int VC = D * BC / 2;
@@ -91,14 +93,16 @@ struct Geo {
   static constexpr int OFF_VC = KC + KS;
   static constexpr int OFF_VS = KC + KS + VC;
   static constexpr int STAGE = KC + KS + VC + VS;
-  static constexpr int CODE_DMA = D / 64;       // 1 KB code loads per wave per tile, for K and for V
+  static constexpr int CODE_DMA = D / 64;        // 1 KB code loads per wave per tile, for K and for V
   static constexpr int NDMA = 2 * CODE_DMA + 1;  // DMA instructions per wave per tile
   static_assert(KC == NW * CODE_DMA * 1024 && VC == NW * CODE_DMA * 1024, "code DMA split");
 };
 
-// The 16 keys of S^T MFMA t (t = 0..7): row r holds key 32(r/4) + 4t + (r%4), so the
-// output lane (query, g) ends up with keys 32g .. 32g + 31 of the tile.
-__device__ __forceinline__ int kappa(int t, int r) { return 32 * (r >> 2) + 4 * t + (r & 3); }
+// Key of row rho of S^T MFMA t: output element v of lane (i, h) is row
+// 8(v/4) + 4h + v%4, which this maps to key 64(t/2) + 32h + 16(t%2) + v.
+__device__ __forceinline__ int kappa(int t, int rho) {
+  return 64 * (t >> 1) + 32 * ((rho >> 2) & 1) + 16 * (t & 1) + 4 * (rho >> 3) + (rho & 3);
+}
 
 // Per-lane byte offsets of a wave's tile DMAs (the same for every tile).
 template <int D>
@@ -114,22 +118,22 @@ __device__ __forceinline__ DmaOffsets<D> dma_offsets(int64_t kv_pad, int wave, i
   DmaOffsets<D> o;
 #pragma unroll
   for (int u = 0; u < G::CODE_DMA; ++u) {
-    const int s = 64 * (G::CODE_DMA * wave + u) + lane;  // 16-byte unit of the K region
-    const int t = s / (16 * G::GK), g = (s / 16) % G::GK, r = s % 16;
-    o.k[u] = (uint32_t)(kappa(t, r) * (D / 2) + 16 * g);
+    const int p = 64 * (G::CODE_DMA * wave + u) + lane;  // 16-byte unit of the K region
+    const int t = p / (64 * G::S), s = (p / 64) % G::S, l = p % 64;
+    o.k[u] = (uint32_t)(kappa(t, l & 31) * (D / 2) + 16 * (2 * s + (l >> 5)));
   }
 #pragma unroll
   for (int u = 0; u < G::CODE_DMA; ++u) {
-    const int s = 64 * (G::CODE_DMA * wave + u) + lane;  // 16-byte unit of the V region
-    const int ct = s / 64, g = (s / 16) % 4, r = s % 16;
-    o.v[u] = (uint32_t)((16 * ct + r) * (kv_pad / 2) + 16 * g);
+    const int p = 64 * (G::CODE_DMA * wave + u) + lane;  // 16-byte unit of the V region
+    const int ct = p / 128, c = (p / 64) % 2, l = p % 64;
+    o.v[u] = (uint32_t)((32 * ct + (l & 31)) * (kv_pad / 2) + 32 * c + 16 * (l >> 5));
   }
   if (wave < 2) {
-    const int p = 64 * wave + lane;  // dword 8 r + t of the K scale region
-    o.s = (uint32_t)(kappa(p % 8, p / 8) * (D / 32));
+    const int p = 64 * wave + lane;  // dword 4 i + t of the K scale region
+    o.s = (uint32_t)(kappa(p % 4, p / 4) * (D / 32));
   } else {
-    const int p = (wave - 2) * (D / 2) + lane;  // dword NCT r + ct of the V scale region
-    const int ch = 16 * (p % G::NCT) + p / G::NCT;
+    const int p = (wave - 2) * (D / 2) + lane;  // dword NCT i + ct of the V scale region
+    const int ch = 32 * (p % G::NCT) + p / G::NCT;
     o.s = (uint32_t)(ch * (kv_pad / 32));
   }
   return o;
@@ -177,9 +181,16 @@ __device__ __forceinline__ void tile_dma(uint8_t* st, const DmaOffsets<D>& o, co
   }
 }
 
-// Gather byte g of each of four dwords (x, y, z, w) into one dword, x in byte 0.
-__device__ __forceinline__ uint32_t gather4(const u32x4& d, uint32_t sel_lo, uint32_t sel_hi) {
-  return __builtin_amdgcn_perm(d.y, d.x, sel_lo) | __builtin_amdgcn_perm(d.w, d.z, sel_hi);
+// v_perm selectors that gather byte b of two dwords into bytes 0-1 (lo) or 2-3 (hi).
+struct Sel {
+  uint32_t lo, hi;
+};
+__device__ __forceinline__ Sel byte_sel(uint32_t b) {
+  return Sel{b | ((b + 4) << 8) | 0x0C0C0000u, 0x00000C0Cu | (b << 16) | ((b + 4) << 24)};
+}
+// Gather byte b of each of four dwords (x, y, z, w) into one dword, x in byte 0.
+__device__ __forceinline__ uint32_t gather4(const u32x4& d, Sel s) {
+  return __builtin_amdgcn_perm(d.y, d.x, s.lo) | __builtin_amdgcn_perm(d.w, d.z, s.hi);
 }
 
 // Workgroup barrier that the compiler may not move memory accesses across, without
@@ -194,98 +205,23 @@ __device__ __forceinline__ void stage_barrier() {
 
 __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// Max of the 32 values s[t][jj] with a max3 tree.
-__device__ __forceinline__ float max32(const v4f (&s)[8]) {
+// Max of the 32 values of one block (a = keys 0..15, b = keys 16..31) with a max3 tree.
+__device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
+  auto x = [&](int k) { return k < 16 ? a[k] : b[k - 16]; };
   float u[11];
 #pragma unroll
-  for (int i = 0; i < 10; ++i) {
-    const int a = 3 * i, b = 3 * i + 1, c = 3 * i + 2;
-    u[i] = fmax3(s[a / 4][a % 4], s[b / 4][b % 4], s[c / 4][c % 4]);
-  }
-  u[10] = fmaxf(s[7][2], s[7][3]);
+  for (int i = 0; i < 10; ++i) u[i] = fmax3(x(3 * i), x(3 * i + 1), x(3 * i + 2));
+  u[10] = fmaxf(x(30), x(31));
   const float w0 = fmax3(u[0], u[1], u[2]), w1 = fmax3(u[3], u[4], u[5]);
   const float w2 = fmax3(u[6], u[7], u[8]), w3 = fmaxf(u[9], u[10]);
   return fmaxf(fmax3(w0, w1, w2), w3);
 }
 
-// S^T MFMAs of one 16-query group: s[t][jj] = S(query, key 32 g + 4 t + jj of the tile).
-__device__ __forceinline__ void s_mfma(v4f (&s)[8], const v8i (&kf)[8], const int (&ksw)[2], const v8i& qf,
-                                       int qsc) {
-  const v4f z = v4f{0, 0, 0, 0};
-  s[0] = mma<0>(kf[0], qf, z, ksw[0], qsc);
-  s[1] = mma<1>(kf[1], qf, z, ksw[0], qsc);
-  s[2] = mma<2>(kf[2], qf, z, ksw[0], qsc);
-  s[3] = mma<3>(kf[3], qf, z, ksw[0], qsc);
-  s[4] = mma<0>(kf[4], qf, z, ksw[1], qsc);
-  s[5] = mma<1>(kf[5], qf, z, ksw[1], qsc);
-  s[6] = mma<2>(kf[6], qf, z, ksw[1], qsc);
-  s[7] = mma<3>(kf[7], qf, z, ksw[1], qsc);
-}
-
-// Softmax, plain-ALU part: masks keys past the end (TAIL), updates the running max m
-// from the block max and the row max over the 4 lanes of the query, and turns s into
-// the exponent arguments x = (S - m') * softmax_scale * log2(e).  Returns the block
-// max's argument (bm - m') * cl; alpha = exp2((m - m') cl) is the running-state factor.
-template <bool TAIL>
-__device__ __forceinline__ float soft_alu(v4f (&s)[8], float& m, float cl, int lim, float& alpha) {
-  if constexpr (TAIL) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        if (4 * t + jj >= lim) s[t][jj] = -INFINITY;
-  }
-  const float bm = max32(s);
-  const float mnew = fmaxf(m, xmax4(bm));
-  alpha = __builtin_amdgcn_exp2f((m - mnew) * cl);
-  m = mnew;
-  const float mc = mnew * cl;
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) s[t][jj] = __builtin_fmaf(s[t][jj], cl, -mc);
-  return (bm - mnew) * cl;
-}
-
-// Softmax, transcendental part: P~ = exp2(x) and its PNQ quantisation, once, in the
-// lane's aligned 32-key block.  The block max of P~ is exp2 of the block max's
-// argument (exactly 1 where the block holds the row max).
-__device__ __forceinline__ void soft_exp(const v4f (&x)[8], float xm, Rule prule, float (&p)[32], uint32_t (&pc)[4],
-                                         int& psc) {
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) p[4 * t + jj] = __builtin_amdgcn_exp2f(x[t][jj]);
-  const float pm = __builtin_amdgcn_exp2f(xm);
-  const int e = mx_exponent(__float_as_uint(pm), prule);
-  quant32(p, e, pc);
-  psc = e + 127;
-}
-
-// O~^T += V^^T P^^T for one group, plus the PNQ row sum as a ones MFMA over the same P^.
-template <int D, bool PNQ>
-__device__ __forceinline__ void pv_mfma(v4f (&acc)[D / 16], v4f& accl, const v8i (&vf)[D / 16], const int (&vsw)[2],
-                                        const v8i& ones, const v8i& pf8, int psc) {
-  constexpr int NCT = D / 16;
-  if constexpr (PNQ) accl = mma<0>(ones, pf8, accl, 127, psc);
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    if ((ct & 3) == 0) acc[ct] = mma<0>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
-    if ((ct & 3) == 1) acc[ct] = mma<1>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
-    if ((ct & 3) == 2) acc[ct] = mma<2>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
-    if ((ct & 3) == 3) acc[ct] = mma<3>(vf[ct], pf8, acc[ct], vsw[ct >> 2], psc);
-  }
-}
-
-// Make the compiler produce the eight accumulator tiles at this point of the program
-// (it would otherwise sink work past the branches that follow).
-__device__ __forceinline__ void pin(v4f (&x)[8]) {
-  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
-}
+// Make the compiler produce these values at this point of the program.
+__device__ __forceinline__ void pin(v16f (&x)[4]) { asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])); }
 
 // Interleave the next N MFMAs of the scheduling region with K ALU/transcendental
-// instructions each, so the exponentials and conversions of one group execute in
-// the shadow of the other group's matrix products.
+// instructions each.
 template <int N, int K>
 __device__ __forceinline__ void interleave_mfma() {
 #pragma unroll
@@ -295,216 +231,261 @@ __device__ __forceinline__ void interleave_mfma() {
   }
 }
 
-// One kv tile for one wave's two 16-query groups (q0, q1).  The order overlaps
-// each group's transcendental softmax work with the other group's MFMAs:
-//   S(q0) | ALU(q0) | S(q1) + EXP(q0) | ALU(q1) | rescale | PV(q0) + EXP(q1) | PV(q1)
-// `rem` (TAIL only) is the number of valid keys in the tile.
-template <int D, int QG, bool PNQ, bool DUMP, bool TAIL>
-__device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int lane, uint32_t sel_lo,
-                                            uint32_t sel_hi, int rem, const v8i (&qf)[QG], const int (&qsc)[QG],
-                                            v4f (&acc)[QG][D / 16], v4f (&accl)[QG], float (&m)[QG],
-                                            float (&ldir)[QG], float cl, Rule prule, const AttnArgs& a,
-                                            const int64_t (&qrow)[QG], int64_t head, int j,
-                                            const uint32_t* lones) {
-  static_assert(QG == 2, "the tile schedule pairs two query groups");
-  using G = Geo<D>;
-  constexpr int NCT = G::NCT;
-  const int r = lane & 15;  // query within a 16-group / row within an MFMA tile
-  const int g = lane >> 4;  // 32-wide k block of the MFMA operand
-  const int lim = rem - 32 * g;  // keys of this lane's block that exist (TAIL)
-
-  // K^ fragments: MFMA t uses keys kappa(t, r) as its 16 rows
-  v8i kf[8];
-  int ksw[2];
-  {
-    const bool live = g < G::GK;  // at D = 64 lanes with g >= 2 carry zero operands
+// P~ = exp2(x) of block c (x[2c], x[2c+1]) and its PNQ quantisation: codes pc, scale byte psc.
+// The block max of P~ is exp2 of the block max's argument xm (exactly 1 in the row max's block).
+template <bool PNQ>
+__device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float xm, Rule prule, uint32_t (&pc)[4],
+                                         int& psc, float& ls) {
+  float p[32];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      u32x4 w = u32x4{0u, 0u, 0u, 0u};
-      if (live) w = *reinterpret_cast<const u32x4*>(st + 256 * G::GK * t + 16 * lane);
-      kf[t] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-    }
-    // the scales of keys kappa(0..7, r): byte g of dwords 8r .. 8r + 7
-    const u32x4 s0 = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 32 * r);
-    const u32x4 s1 = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 32 * r + 16);
-    ksw[0] = (int)gather4(s0, sel_lo, sel_hi);
-    ksw[1] = (int)gather4(s1, sel_lo, sel_hi);
+  for (int k = 0; k < 16; ++k) {
+    p[k] = __builtin_amdgcn_exp2f(xa[k]);
+    p[16 + k] = __builtin_amdgcn_exp2f(xb[k]);
   }
-
-  v4f s0[8], s1[8];
-  float alpha0, alpha1, p[32];
-  int psc0, psc1;
-  uint32_t pc0[4], pc1[4];
-
-  s_mfma(s0, kf, ksw, qf[0], qsc[0]);
-  const float xm0 = soft_alu<TAIL>(s0, m[0], cl, lim, alpha0);
-  pin(s0);
-  __builtin_amdgcn_sched_barrier(0);
-  s_mfma(s1, kf, ksw, qf[1], qsc[1]);
-  soft_exp(s0, xm0, prule, p, pc0, psc0);
+  const float pm = __builtin_amdgcn_exp2f(xm);
+  psc = mx_scale_byte(__float_as_uint(pm), prule);
+  quant32(p, psc, pc);
   if constexpr (!PNQ) {
-    float ls = 0.0f;
 #pragma unroll
     for (int k = 0; k < 32; ++k) ls += p[k];
-    ldir[0] = ldir[0] * alpha0 + xsum4(ls);
   }
-  interleave_mfma<8, 6>();
-  // keep group 0's quantisation here: its only consumers come after the rescale
-  // branches below, past which the compiler would otherwise sink it
-  asm volatile("" : "+v"(pc0[0]), "+v"(pc0[1]), "+v"(pc0[2]), "+v"(pc0[3]), "+v"(psc0));
-  __builtin_amdgcn_sched_barrier(0);
-  const float xm1 = soft_alu<TAIL>(s1, m[1], cl, lim, alpha1);
-  pin(s1);
+}
 
-  // V^ fragments (A operand of O^T): channels 16 ct + r, keys 32 g .. 32 g + 31
-  v8i vf[NCT];
-  int vsw[2];
-  {
+// O~^T += V^^T P^^T for 64-key chunk c, plus (PNQ) the row sum of the same P^ as a ones MFMA.
+template <int D, bool PNQ>
+__device__ __forceinline__ void pv_mfma(v16f (&acc)[D / 32], v16f& rs, const v8i (&vf)[D / 32][2], int vsw,
+                                        const v8i& ones, const uint32_t (&pc)[4], int psc, int c) {
+  constexpr int NCT = D / 32;
+  const v8i pf = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
+  if constexpr (PNQ) rs = mma<0>(ones, pf, rs, 127, psc);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(st + G::OFF_VC + 1024 * ct + 16 * lane);
-      vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (ct == 0) acc[ct] = mma<0>(vf[ct][c], pf, acc[ct], vsw, psc);
+    if (ct == 1) acc[ct] = mma<1>(vf[ct][c], pf, acc[ct], vsw, psc);
+    if (ct == 2) acc[ct] = mma<2>(vf[ct][c], pf, acc[ct], vsw, psc);
+    if (ct == 3) acc[ct] = mma<3>(vf[ct][c], pf, acc[ct], vsw, psc);
+  }
+}
+
+// One kv tile for one wave's 32 queries.  `rem` (TAIL only) is the number of valid
+// keys in the tile.
+template <int D, bool PNQ, bool DUMP, bool TAIL>
+__device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int lane, Sel sel0, Sel sel1, int rem,
+                                            const v8i (&qf)[D / 64], const int (&qsc)[D / 64],
+                                            v16f (&acc)[D / 32], float& m, float& l, float cl, Rule prule,
+                                            const AttnArgs& a, int64_t qrow, int64_t head, int j,
+                                            const uint32_t* lones) {
+  using G = Geo<D>;
+  constexpr int S = G::S;
+  constexpr int NCT = G::NCT;
+  const int i = lane & 31;
+  const int h = lane >> 5;
+
+  // K^ fragments and scales: MFMA (t, s) uses keys kappa(t, .), d-block 2s + h
+  v8i kf[4][S];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(st + 1024 * (S * t + s) + 16 * lane);
+      kf[t][s] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
-    // the scales of channels 16 ct + r: byte g of dwords NCT r .. NCT r + NCT - 1
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r);
-    vsw[0] = (int)gather4(v0, sel_lo, sel_hi);
-    if constexpr (NCT > 4) {
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 4 * NCT * r + 16);
-      vsw[1] = (int)gather4(v1, sel_lo, sel_hi);
-    } else {
-      vsw[1] = 0;
+  int ksw[S];
+  {
+    const u32x4 d = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 16 * i);
+    ksw[0] = (int)gather4(d, sel0);
+    if constexpr (S == 2) ksw[1] = (int)gather4(d, sel1);
+  }
+
+  const v16f z = {};
+  v16f x[4];
+  x[0] = mma<0>(kf[0][0], qf[0], z, ksw[0], qsc[0]);
+  x[1] = mma<1>(kf[1][0], qf[0], z, ksw[0], qsc[0]);
+  if constexpr (S == 2) {
+    x[0] = mma<0>(kf[0][1], qf[1], x[0], ksw[1], qsc[1]);
+    x[1] = mma<1>(kf[1][1], qf[1], x[1], ksw[1], qsc[1]);
+  }
+  x[2] = mma<2>(kf[2][0], qf[0], z, ksw[0], qsc[0]);
+  x[3] = mma<3>(kf[3][0], qf[0], z, ksw[0], qsc[0]);
+  if constexpr (S == 2) {
+    x[2] = mma<2>(kf[2][1], qf[1], x[2], ksw[1], qsc[1]);
+    x[3] = mma<3>(kf[3][1], qf[1], x[3], ksw[1], qsc[1]);
+  }
+
+  if constexpr (TAIL) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int lim = rem - 64 * (t >> 1) - 32 * h - 16 * (t & 1);
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (v >= lim) x[t][v] = -INFINITY;
     }
+  }
+  const float bm0 = max32(x[0], x[1]);
+  const float bm1 = max32(x[2], x[3]);
+  const float mnew = fmaxf(m, xmax2(fmaxf(bm0, bm1)));
+  const float alpha = __builtin_amdgcn_exp2f((m - mnew) * cl);
+  m = mnew;
+  const float mc = mnew * cl;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) x[t][v] = __builtin_fmaf(x[t][v], cl, -mc);
+  const float xm0 = (bm0 - mnew) * cl, xm1 = (bm1 - mnew) * cl;
+
+  // V^ fragments (A operand of O^T): channels 32 ct + i, keys 64 c + 32 h .. +31
+  v8i vf[NCT][2];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(st + G::OFF_VC + 1024 * (2 * ct + c) + 16 * lane);
+      vf[ct][c] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+    }
+  int vsw[2];
+  if constexpr (NCT == 4) {
+    const u32x4 d = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 16 * i);
+    vsw[0] = (int)gather4(d, sel0);
+    vsw[1] = (int)gather4(d, sel1);
+  } else {
+    const u32x2 d = *reinterpret_cast<const u32x2*>(st + G::OFF_VS + 8 * i);
+    vsw[0] = (int)__builtin_amdgcn_perm(d.y, d.x, sel0.lo);
+    vsw[1] = (int)__builtin_amdgcn_perm(d.y, d.x, sel1.lo);
   }
   v8i ones;
   {
-    // all-ones fp4 operand (code 0x2 = 1.0) for the PNQ row sum, read from LDS so it
-    // does not occupy registers outside this phase
     const u32x4 w = *reinterpret_cast<const u32x4*>(lones);
     ones = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
   }
-  // rescale the running state of a group when any of its rows' max moved (alpha == 1 is exact)
-  if (__builtin_amdgcn_ballot_w64(alpha0 != 1.0f)) {
+
+  uint32_t pc0[4], pc1[4];
+  int psc0, psc1;
+  float ls = 0.0f;
+  soft_exp<PNQ>(x[0], x[1], xm0, prule, pc0, psc0, ls);
+
+  // rescale the running state when any row's max moved (alpha == 1 is exact)
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[0][ct] *= alpha0;
-    accl[0] *= alpha0;
-  }
-  if (__builtin_amdgcn_ballot_w64(alpha1 != 1.0f)) {
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[1][ct] *= alpha1;
-    accl[1] *= alpha1;
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] *= alpha;
   }
   __builtin_amdgcn_sched_barrier(0);
-  pv_mfma<D, PNQ>(acc[0], accl[0], vf, vsw, ones, v8i{(int)pc0[0], (int)pc0[1], (int)pc0[2], (int)pc0[3], 0, 0, 0, 0},
-                  psc0);
-  soft_exp(s1, xm1, prule, p, pc1, psc1);
-  if constexpr (!PNQ) {
-    float ls = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) ls += p[k];
-    ldir[1] = ldir[1] * alpha1 + xsum4(ls);
-  }
-  interleave_mfma<NCT + 1, 6>();
+  v16f rs = z;
+  pv_mfma<D, PNQ>(acc, rs, vf, vsw[0], ones, pc0, psc0, 0);
+  soft_exp<PNQ>(x[2], x[3], xm1, prule, pc1, psc1, ls);
+  interleave_mfma<NCT + (PNQ ? 1 : 0), 6>();
   __builtin_amdgcn_sched_barrier(0);
-  pv_mfma<D, PNQ>(acc[1], accl[1], vf, vsw, ones, v8i{(int)pc1[0], (int)pc1[1], (int)pc1[2], (int)pc1[3], 0, 0, 0, 0},
-                  psc1);
+  pv_mfma<D, PNQ>(acc, rs, vf, vsw[1], ones, pc1, psc1, 1);
+  if constexpr (PNQ) l = __builtin_fmaf(l, alpha, rs[0]);
+  else l = __builtin_fmaf(l, alpha, xsum2(ls));
 
   if constexpr (DUMP) {
-    const uint32_t* pcs[2] = {pc0, pc1};
-    const int pscs[2] = {psc0, psc1};
+    if (qrow < a.nq) {
+      const int64_t prow = head * a.nq + qrow;
+      const uint32_t* pcs[2] = {pc0, pc1};
+      const int pscs[2] = {psc0, psc1};
 #pragma unroll
-    for (int qg = 0; qg < 2; ++qg) {
-      if (qrow[qg] < a.nq) {
-        const int64_t prow = head * a.nq + qrow[qg];
-        const int64_t key0 = (int64_t)j * BC + 32 * g;
+      for (int c = 0; c < 2; ++c) {
+        const int64_t key0 = (int64_t)j * BC + 64 * c + 32 * h;
         *reinterpret_cast<uint4*>(a.pc + prow * (a.kv_pad / 2) + key0 / 2) =
-            make_uint4(pcs[qg][0], pcs[qg][1], pcs[qg][2], pcs[qg][3]);
-        a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)pscs[qg];
+            make_uint4(pcs[c][0], pcs[c][1], pcs[c][2], pcs[c][3]);
+        a.ps[prow * (a.kv_pad / 32) + key0 / 32] = (uint8_t)pscs[c];
       }
     }
   }
 }
 
-// Fused Q quantisation (mxattn_forward): lane (r, g) turns elements 32g .. 32g + 31 of
-// query row `row` into one MXFP4 block exactly as the standalone quantiser does -- the
-// fp32 butterflies h = 1, 2, ..., d/2 (pairs (i, i + h) -> (a + b, a - b)), one multiply
-// by fl32(1/sqrt d), the block max, the shared exponent and the rounding conversion --
-// so the codes are bit-identical to mxattn_quantize's.  Butterflies h = 1..16 run in the
-// lane; h = 32 and h = 64 pair the lanes holding blocks g ^ 1 and g ^ 2 (16 and 32 lanes
-// apart).  Every lane of the wave takes part in the exchanges; lanes with g >= d/32 hold
-// zeros and produce code 0 with scale 127.
+// Fused Q quantisation (mxattn_forward): lane (i, h) turns elements 32(2s + h) ..
+// +31, s = 0..d/64-1, of query row `row` into MXFP4 blocks exactly as the standalone
+// quantiser does -- the fp32 butterflies h = 1, 2, ..., d/2 (pairs (k, k + h) ->
+// (a + b, a - b)), one multiply by fl32(1/sqrt d), the block max, the shared exponent
+// and the rounding conversion -- so the codes are bit-identical to mxattn_quantize's.
+// Butterflies 1..16 run inside each block, 32 pairs the lanes 32 apart (blocks 2s and
+// 2s + 1), and 64 pairs the lane's own two blocks.
 template <int D>
-__device__ __forceinline__ void quantise_q_block(const AttnArgs& a, int64_t row, int g, Rule rule,
-                                                 uint32_t (&w)[4], int& sc) {
-  constexpr int GK = D / 32;
-  float v[32];
-  if (g < GK) {
+__device__ __forceinline__ void quantise_q_blocks(const AttnArgs& a, int64_t row, int h, Rule rule,
+                                                  uint32_t (&w)[D / 64][4], int (&sc)[D / 64]) {
+  constexpr int S = D / 64;
+  float v[S][32];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int e0 = 32 * (2 * s + h);
     if (a.q_bf16) {
-      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.qraw) + row * D + 32 * g);
+      const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.qraw) + row * D + e0);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint4 u = src[k];
-        v[8 * k + 0] = bf16lo(u.x); v[8 * k + 1] = bf16hi(u.x);
-        v[8 * k + 2] = bf16lo(u.y); v[8 * k + 3] = bf16hi(u.y);
-        v[8 * k + 4] = bf16lo(u.z); v[8 * k + 5] = bf16hi(u.z);
-        v[8 * k + 6] = bf16lo(u.w); v[8 * k + 7] = bf16hi(u.w);
+        v[s][8 * k + 0] = bf16lo(u.x); v[s][8 * k + 1] = bf16hi(u.x);
+        v[s][8 * k + 2] = bf16lo(u.y); v[s][8 * k + 3] = bf16hi(u.y);
+        v[s][8 * k + 4] = bf16lo(u.z); v[s][8 * k + 5] = bf16hi(u.z);
+        v[s][8 * k + 6] = bf16lo(u.w); v[s][8 * k + 7] = bf16hi(u.w);
       }
     } else {
-      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.qraw) + row * D + 32 * g);
+      const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.qraw) + row * D + e0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float4 u = src[k];
-        v[4 * k + 0] = u.x; v[4 * k + 1] = u.y; v[4 * k + 2] = u.z; v[4 * k + 3] = u.w;
+        v[s][4 * k + 0] = u.x; v[s][4 * k + 1] = u.y; v[s][4 * k + 2] = u.z; v[s][4 * k + 3] = u.w;
       }
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
   }
   if (a.q_hadamard) {
 #pragma unroll
-    for (int h = 1; h < 32; h *= 2) {
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        if ((i & h) == 0) {
-          const float x = v[i], y = v[i + h];
-          v[i] = x + y;
-          v[i + h] = x - y;
-        }
+      for (int hh = 1; hh < 32; hh *= 2)
+#pragma unroll
+        for (int k = 0; k < 32; ++k)
+          if ((k & hh) == 0) {
+            const float x = v[s][k], y = v[s][k + hh];
+            v[s][k] = x + y;
+            v[s][k + hh] = x - y;
+          }
+    // h = 32: the partner lane holds the other block of the pair; the lane with the
+    // higher block takes partner - own
+    const uint32_t sgn = h ? 0x80000000u : 0u;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float p = __shfl_xor(v[s][k], 32);
+        v[s][k] = p + __uint_as_float(__float_as_uint(v[s][k]) ^ sgn);
+      }
+    if constexpr (S == 2) {  // h = 64: elements k of blocks h and 2 + h
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float x = v[0][k], y = v[1][k];
+        v[0][k] = x + y;
+        v[1][k] = x - y;
       }
     }
 #pragma unroll
-    for (int st = 1; st < GK; st *= 2) {  // h = 32 st: the partner holds block g ^ st
-      const uint32_t sgn = (uint32_t)(g & st) != 0 ? 0x80000000u : 0u;
+    for (int s = 0; s < S; ++s)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float p = __shfl_xor(v[i], 16 * st);
-        v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ sgn);  // a + b, or b-lane: a + (-b)
-      }
+      for (int k = 0; k < 32; ++k) v[s][k] = v[s][k] * a.q_c;
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    // integer max of |bits| (this file is built assuming no NaNs, so no float max here):
+    // NaN and Inf sort above every finite value
+    uint32_t mb = 0;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) mb = max(mb, __float_as_uint(v[s][k]) & 0x7FFFFFFFu);
+    w[s][0] = w[s][1] = w[s][2] = w[s][3] = 0u;
+    if (mb >= 0x7F800000u) {
+      sc[s] = 0xFF;  // a non-finite block: codes 0, scale NaN, as the quantiser writes it
+    } else {
+      sc[s] = mx_scale_byte(mb, rule);
+      quant32(v[s], sc[s], w[s]);
     }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = v[i] * a.q_c;
   }
-  if (g >= GK) return;
-  // integer max of |bits| (this file is built assuming no NaNs, so no float max here):
-  // NaN and Inf sort above every finite value
-  uint32_t mb = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) mb = max(mb, __float_as_uint(v[i]) & 0x7FFFFFFFu);
-  if (mb >= 0x7F800000u) {
-    sc = 0xFF;  // a non-finite block: codes 0, scale NaN, as the quantiser writes it
-    return;
-  }
-  const int e = mx_exponent(mb, rule);
-  quant32(v, e, w);
-  sc = e + 127;
 }
 
-// One workgroup = NW waves; wave w owns QG groups of 16 queries.
-template <int D, int QG, bool PNQ, bool DUMP>
+// One workgroup = NW waves of 32 queries.
+template <int D, bool PNQ, bool DUMP>
 __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   using G = Geo<D>;
-  constexpr int NCT = G::NCT;       // 16-channel tiles of O
-  constexpr int BR = 16 * QG * NW;  // queries per workgroup
+  constexpr int S = G::S;
+  constexpr int NCT = G::NCT;
   // three tile stages, declared apart so the compiler can tell a DMA into one
   // stage from reads of another and keeps the DMA in flight across those reads
   __shared__ __attribute__((aligned(16))) uint8_t st0[G::STAGE];
@@ -525,12 +506,10 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int r = lane & 15;
-  const int g = lane >> 4;
+  const int i = lane & 31;
+  const int h = lane >> 5;
   const int nkv = (int)a.nkv;
-  // v_perm selectors that pick byte g of two dwords (low and high halves of gather4)
-  const uint32_t sel_lo = (uint32_t)g | ((uint32_t)(g + 4) << 8) | 0x0C0C0000u;
-  const uint32_t sel_hi = 0x00000C0Cu | ((uint32_t)g << 16) | ((uint32_t)(g + 4) << 24);
+  const Sel sel0 = byte_sel((uint32_t)h), sel1 = byte_sel((uint32_t)(2 + h));
 
   const uint8_t* qc = a.qc + head * a.nq * (D / 2);
   const uint8_t* qs = a.qs + head * a.nq * (D / 32);
@@ -539,42 +518,38 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
                     a.vc + head * (int64_t)D * (kvp / 2), a.vs + head * (int64_t)D * (kvp / 32),
                     nkv * (D / 2), nkv * (D / 32), D * (kvp / 2), D * (kvp / 32)};
 
-  // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop: lane (r, g) holds
-  // block g of query row r.  Either read from the quantised Q^, or made here from the
-  // raw query rows (the fused prologue of mxattn_forward), see quantise_q_block.
-  v8i qf[QG];
-  int qsc[QG];
-  int64_t qrow[QG];
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    int64_t q = (int64_t)qt * BR + wave * (16 * QG) + qg * 16 + r;
-    qrow[qg] = q;
-    const int64_t qq = q < a.nq ? q : a.nq - 1;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    int sc = 127;
+  // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop: lane (i, h) holds
+  // blocks 2s + h of query row i.  Either read from the quantised Q^, or made here
+  // from the raw query rows (the fused prologue of mxattn_forward).
+  const int64_t qrow = (int64_t)qt * BR + wave * 32 + i;
+  const int64_t qq = qrow < a.nq ? qrow : a.nq - 1;
+  v8i qf[S];
+  int qsc[S];
+  {
+    uint32_t w[S][4];
+    int sc[S];
     if (a.qraw) {
-      quantise_q_block<D>(a, head * a.nq + qq, g, prule, w, sc);
-    } else if (g < G::GK) {
-      const uint4 u = *reinterpret_cast<const uint4*>(qc + qq * (D / 2) + 16 * g);
-      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-      sc = qs[qq * (D / 32) + g];
+      quantise_q_blocks<D>(a, head * a.nq + qq, h, prule, w, sc);
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint4 u = *reinterpret_cast<const uint4*>(qc + qq * (D / 2) + 16 * (2 * s + h));
+        w[s][0] = u.x; w[s][1] = u.y; w[s][2] = u.z; w[s][3] = u.w;
+        sc[s] = qs[qq * (D / 32) + 2 * s + h];
+      }
     }
-    qf[qg] = v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
-    qsc[qg] = sc;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      qf[s] = v8i{(int)w[s][0], (int)w[s][1], (int)w[s][2], (int)w[s][3], 0, 0, 0, 0};
+      qsc[s] = sc[s];
+    }
   }
 
-  // ---- online-softmax state
-  v4f acc[QG][NCT];
-  v4f accl[QG];
-  float m[QG], ldir[QG];
+  // ---- online-softmax state: lane (i, h) holds channels 32 ct + 8(v/4) + 4h + v%4
+  v16f acc[NCT];
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    m[qg] = -INFINITY;
-    ldir[qg] = 0.0f;
-    accl[qg] = v4f{0, 0, 0, 0};
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[qg][ct] = v4f{0, 0, 0, 0};
-  }
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = v16f{};
+  float m = -INFINITY, l = 0.0f;
   const float cl = a.scale_log2;
   const int ntiles = (nkv + BC - 1) / BC;
   const int nfull = nkv / BC;  // tiles with no padded key
@@ -602,50 +577,45 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
     sj = sj == 2 ? 0 : sj + 1;
     return cur;
   };
-  // The loop is not unrolled over the three stages: the stage pointers are then
-  // run-time values, and the compiler adds a wait for the DMAs of the previous tile
-  // (issued a whole tile earlier) before the first read, never for the ones just issued.
   int j = 0;
   for (; j < nfull; ++j) {
     const uint8_t* cur = enter(j);
-    attend_tile<D, QG, PNQ, DUMP, false>(cur, lane, sel_lo, sel_hi, BC, qf, qsc, acc, accl, m, ldir, cl, prule,
-                                         a, qrow, head, j, lones);
+    attend_tile<D, PNQ, DUMP, false>(cur, lane, sel0, sel1, BC, qf, qsc, acc, m, l, cl, prule, a, qrow, head, j,
+                                     lones);
   }
   if (j < ntiles) {  // the ragged last tile, masked
     const uint8_t* cur = enter(j);
-    attend_tile<D, QG, PNQ, DUMP, true>(cur, lane, sel_lo, sel_hi, nkv - j * BC, qf, qsc, acc, accl, m, ldir, cl,
-                                        prule, a, qrow, head, j, lones);
+    attend_tile<D, PNQ, DUMP, true>(cur, lane, sel0, sel1, nkv - j * BC, qf, qsc, acc, m, l, cl, prule, a, qrow,
+                                    head, j, lones);
   }
   MX_VMCNT(0);  // no DMA may still target this workgroup's LDS when it exits
 
-  // ---- epilogue: O = O~ / l ; lane holds channels 16ct + 4g + jj of its query
-#pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    if (qrow[qg] >= a.nq) continue;
-    const float l = PNQ ? accl[qg][0] : ldir[qg];
+  // ---- epilogue: O = O~ / l
+  if (qrow < a.nq) {
     const float inv = 1.0f / l;
-    const int64_t orow = head * a.nq + qrow[qg];
+    const int64_t orow = head * a.nq + qrow;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int ch = 16 * ct + 4 * g;
-      const float o0 = acc[qg][ct][0] * inv, o1 = acc[qg][ct][1] * inv;
-      const float o2 = acc[qg][ct][2] * inv, o3 = acc[qg][ct][3] * inv;
-      if (a.out_bf16) {
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + orow * D + ch;
-        const uint32_t w0 = f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
-        const uint32_t w1 = f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
-        *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
-      } else {
-        float* op = reinterpret_cast<float*>(a.o) + orow * D + ch;
-        *reinterpret_cast<float4*>(op) = make_float4(o0, o1, o2, o3);
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int ch = 32 * ct + 8 * b + 4 * h;
+        const float o0 = acc[ct][4 * b] * inv, o1 = acc[ct][4 * b + 1] * inv;
+        const float o2 = acc[ct][4 * b + 2] * inv, o3 = acc[ct][4 * b + 3] * inv;
+        if (a.out_bf16) {
+          uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + orow * D + ch;
+          const uint32_t w0 = f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
+          const uint32_t w1 = f32_to_bf16_rne(o2) | ((uint32_t)f32_to_bf16_rne(o3) << 16);
+          *reinterpret_cast<uint2*>(op) = make_uint2(w0, w1);
+        } else {
+          float* op = reinterpret_cast<float*>(a.o) + orow * D + ch;
+          *reinterpret_cast<float4*>(op) = make_float4(o0, o1, o2, o3);
+        }
       }
-    }
   }
 }
 
-template <int D, int QG>
-static hipError_t launch_dq(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) {
-  constexpr int BR = 16 * QG * NW;
+template <int D>
+static hipError_t launch_d(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) {
   const int qtiles = (int)((a.nq + BR - 1) / BR);
   const int64_t nb = (int64_t)qtiles * a.heads;
   if (nb > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
@@ -653,19 +623,19 @@ static hipError_t launch_dq(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) 
   const unsigned grid = (unsigned)((nblocks + 7) / 8 * 8);
   const bool dump = a.pc != nullptr;
   if (pnq && !dump)
-    hipLaunchKernelGGL((k_attn<D, QG, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else if (pnq && dump)
-    hipLaunchKernelGGL((k_attn<D, QG, true, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, true, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else if (!dump)
-    hipLaunchKernelGGL((k_attn<D, QG, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else
-    hipLaunchKernelGGL((k_attn<D, QG, false, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, false, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, int d, int pnq, Rule p_rule, hipStream_t s) {
-  if (d == 128) return launch_dq<128, 2>(a, pnq, p_rule, s);
-  if (d == 64) return launch_dq<64, 2>(a, pnq, p_rule, s);
+  if (d == 128) return launch_d<128>(a, pnq, p_rule, s);
+  if (d == 64) return launch_d<64>(a, pnq, p_rule, s);
   return hipErrorInvalidValue;
 }
 

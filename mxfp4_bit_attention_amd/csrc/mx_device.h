@@ -14,25 +14,29 @@
 
 namespace mxattn {
 
-// Shared exponent for a block whose max magnitude has fp32 bit pattern `mbits`
-// (finite, non-negative; zero and subnormals allowed).
+// E8M0 scale byte (shared exponent e plus the bias 127) for a block whose max
+// magnitude has fp32 bit pattern `mbits` (finite, non-negative; zero and subnormals
+// allowed).
 //  CEIL(q): the smallest e with M <= q 2^e.  With M = 1.f 2^E and q = 1.g 2^qe,
 //           that is E - qe when f <= g and E - qe + 1 otherwise.
 //  OCP:     E - 2 (encoded as qe = 2 with a g that no f exceeds).
-// The result is clamped to [-127, 127].  Every M below 2^-126 (zero and
+// e is clamped to [-127, 127], the byte to [0, 254].  Every M below 2^-126 (zero and
 // subnormals included) needs e <= -127 under any rule with q >= 4, so reading E
 // from the biased exponent field (E = -127 for those) and clamping is exact.
-__device__ __forceinline__ int mx_exponent(uint32_t mbits, Rule r) {
-  const int E = (int)(mbits >> 23) - 127;
-  const uint32_t f = mbits & 0x7FFFFFu;
-  const int e = E - r.q_exp + (f > r.q_frac ? 1 : 0);
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
+// Branch-free: adding 2^23 - 1 - g to the bits carries into the exponent field
+// exactly when f > g, and the subtraction of qe is folded into the same constant
+// (q <= 8, so the sum never overflows), leaving an add, a shift and a clamp.
+__device__ __forceinline__ int mx_scale_byte(uint32_t mbits, Rule r) {
+  const uint32_t carry = r.q_frac >= 0x7FFFFFu ? 0u : 0x7FFFFFu - r.q_frac;
+  const int t = (int)(mbits + (carry - ((uint32_t)r.q_exp << 23)));
+  const int eb = t >> 23;  // arithmetic shift: E + 127 - qe + (f > g), rounded down
+  return eb < 0 ? 0 : (eb > 254 ? 254 : eb);
 }
 
-// The conversion's scale operand for shared exponent e: an fp32 whose exponent
-// field is e + 127 (the instruction uses only that field, as an E8M0 value; the
-// field 0 stands for 2^-127 and subnormal inputs convert exactly).
-__device__ __forceinline__ float e8m0_scale(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+// The conversion's scale operand for scale byte eb: an fp32 whose exponent field is
+// eb (the instruction uses only that field, as an E8M0 value; the field 0 stands for
+// 2^-127 and subnormal inputs convert exactly).
+__device__ __forceinline__ float e8m0_scale(int eb) { return __uint_as_float((uint32_t)eb << 23); }
 
 // Two fp32 values -> one byte of two E2M1 codes (a in the low nibble) written
 // into byte `SEL` of `old`, after dividing by 2^e (e from the scale operand).
@@ -41,10 +45,10 @@ __device__ __forceinline__ uint32_t cvt_pk_fp4(uint32_t old, float a, float b, f
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
-// Quantise 32 fp32 values v[0..31] with shared exponent e (any e in [-127, 127])
-// into 4 dwords of codes, element k in nibble k of the 16 bytes.
-__device__ __forceinline__ void quant32(const float* v, int e, uint32_t out[4]) {
-  const float s = e8m0_scale(e);
+// Quantise 32 fp32 values v[0..31] with scale byte eb (any eb in [0, 254]) into
+// 4 dwords of codes, element k in nibble k of the 16 bytes.
+__device__ __forceinline__ void quant32(const float* v, int eb, uint32_t out[4]) {
+  const float s = e8m0_scale(eb);
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     // all four bytes of r are written below, so its initial value is irrelevant:

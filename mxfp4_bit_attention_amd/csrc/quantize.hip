@@ -27,9 +27,9 @@ namespace mxattn {
 // blocks left out as non-finite.  Per-block sums are fp32, the running sums fp64.
 struct ErrAcc {
   double e2 = 0.0, r2 = 0.0, nf = 0.0;
-  __device__ __forceinline__ void add(const float* v, const uint32_t (&q)[4], int e) {
+  __device__ __forceinline__ void add(const float* v, const uint32_t (&q)[4], int eb) {
     typedef float v2f __attribute__((ext_vector_type(2)));
-    const float s = e8m0_scale(e);
+    const float s = e8m0_scale(eb);
     float se = 0.0f, sr = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -210,10 +210,10 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
       if (mh < 0x7F800000u) {
         // max |fl(v c)| = fl(max|v| c), since rounding is monotone
         const uint32_t mb = __float_as_uint(__uint_as_float(mh) * c);
-        const int e = mx_exponent(mb, rule);
-        quant32(blk, e, q[b]);
-        sbyte = (uint32_t)(e + 127);
-        if (ERR && chunk * G::RW + lr < nrows) acc.add(blk, q[b], e);
+        const int eb = mx_scale_byte(mb, rule);
+        quant32(blk, eb, q[b]);
+        sbyte = (uint32_t)eb;
+        if (ERR && chunk * G::RW + lr < nrows) acc.add(blk, q[b], eb);
       } else if (ERR && chunk * G::RW + lr < nrows) {
         acc.nf += 1.0;
       }
@@ -263,10 +263,10 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
     sb = 0xFF;
     if (ERR && valid) acc.nf = 1.0;
   } else {
-    const int e = mx_exponent(mb, rule);
-    quant32(v, e, q);
-    sb = (uint8_t)(e + 127);
-    if (ERR && valid) acc.add(v, q, e);
+    const int eb = mx_scale_byte(mb, rule);
+    quant32(v, eb, q);
+    sb = (uint8_t)eb;
+    if (ERR && valid) acc.add(v, q, eb);
   }
   if constexpr (ERR) {
     acc.flush(err);
@@ -362,10 +362,10 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
       sb = 0xFF;
       if (ERR) acc.nf += 1.0;
     } else {
-      const int e = mx_exponent(mb, rule);
-      quant32(v, e, q);
-      sb = (uint8_t)(e + 127);
-      if (ERR) acc.add(v, q, e);
+      const int eb = mx_scale_byte(mb, rule);
+      quant32(v, eb, q);
+      sb = (uint8_t)eb;
+      if (ERR) acc.add(v, q, eb);
     }
     if constexpr (!ERR) {
       const int64_t crow = b * cols + col + s;
