@@ -3,13 +3,15 @@
 
 One step = the whole hot path on the Wan2.2-720p-shaped self-attention
 (B=1, H=40, N_q=N_kv=75,600, d=128, bf16 inputs resident in HBM): Hadamard +
-UOS quantisation of K along d, UOS quantisation of V along tokens, and the fused
-MXFP4 flash attention with PNQ, which rotates and quantises Q itself as it loads
-its query rows.  Throughput is 4 B H N_q N_kv d per step time, in TFLOP/s.
+UOS quantisation of K along d, UOS quantisation of V along tokens, the re-ordering
+of their scale bytes into the attention kernel's per-tile operand order, and the
+fused MXFP4 flash attention with PNQ, which rotates and quantises Q itself as it
+loads its query rows.  Throughput is 4 B H N_q N_kv d per step time, in TFLOP/s.
 
 Printed as one JSON line, with:
   roofline       the attention kernel (dominant) against the dense MXFP4 MFMA
-                 peak, timed alone with HIP events on its stream, plus HBM
+                 peak, timed alone (through mxattn_forward_arranged, the same
+                 kernel binary) with HIP events on its stream, plus HBM
                  traffic from the committed rocprofv3 counter summary when it
                  was taken on the current kernel source (else null);
   quantize_pass  the standalone Hadamard + quantise pass on 40 x 75,600 x 128
@@ -232,17 +234,19 @@ def main():
     ws = torch.empty(mx.mxattn_forward_workspace_bytes(w.B, w.H, w.N, w.N, w.d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    # attention-only operands (the same kernel mxattn_forward ends with)
+    # attention-only operands: mxattn_forward_arranged launches the kernel mxattn_forward
+    # ends with (same binary; Q^ read instead of quantised in its prologue)
     qc, qs = mx.mxattn_quantize(q.view(-1, w.N, w.d), rule="uos", axis="last", hadamard=True)
     kc, ks = mx.mxattn_quantize(k.view(-1, w.N, w.d), rule="uos", axis="last", hadamard=True)
     vc, vs = mx.mxattn_quantize(v.view(-1, w.N, w.d), rule="uos", axis="rows")
     shp = (w.B, w.H)
     qc, qs, kc, ks = (t.view(*shp, *t.shape[1:]) for t in (qc, qs, kc, ks))
     vc, vs = (t.view(*shp, *t.shape[1:]) for t in (vc, vs))
+    ksa, vsa = mx.mxattn_arrange_scales(ks, vs, w.N)
     out_a = torch.empty_like(q)
 
     def attn_only():
-        mx.mxattn_forward_quantized(qc, qs, kc, ks, vc, vs, w.N, scale, pnq=True, p_rule="uos", out=out_a)
+        mx.mxattn_forward_arranged(qc, qs, kc, ksa, vc, vsa, w.N, scale, pnq=True, p_rule="uos", out=out_a)
 
     if args.traffic_probe:
         # a plain copy of known size (the counter scale reference), then one attention launch
@@ -276,7 +280,7 @@ def main():
     abytes = attn_algorithmic_bytes(w)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4), "traffic": read_traffic(abytes),
-                "kernel": "k_attn<128,PNQ>", "ms_per_launch": round(ms_attn, 3),
+                "kernel": "k_attn<d=128, arranged scales, PNQ>", "ms_per_launch": round(ms_attn, 3),
                 "algorithmic_bytes": abytes}
 
     result = {
@@ -291,7 +295,7 @@ def main():
         "wall_ms_per_step": round(t_wall, 3),
         "roofline": roofline,
     }
-    del qc, qs, kc, ks, vc, vs
+    del qc, qs, kc, ks, vc, vs, ksa, vsa
 
     if not args.no_quantize_pass:
         qw = synth.QUANT_720P

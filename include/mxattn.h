@@ -125,10 +125,10 @@ int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows
                        int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
                        double* sums, void* stream);
 
-/* Bytes of workspace mxattn_forward needs: the quantised K (along d) and the
- * transposed quantised V (along tokens), each piece 256-byte aligned (Q is
- * rotated and quantised inside the attention kernel and never stored).  Returns 0
- * for invalid sizes. */
+/* Bytes of workspace mxattn_forward needs: the quantised K (along d), the
+ * transposed quantised V (along tokens) and both scale sets in the order of
+ * mxattn_arrange_scales, each piece 256-byte aligned (Q is rotated and quantised
+ * inside the attention kernel and never stored).  Returns 0 for invalid sizes. */
 size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d);
 
 /*
@@ -179,6 +179,42 @@ int mxattn_forward_quantized(const uint8_t* Qc, const uint8_t* Qs,
                              int32_t p_rule_kind, float p_qmax,
                              void* O, int32_t out_dtype,
                              uint8_t* p_codes, uint8_t* p_scales, void* stream);
+
+/*
+ * mxattn_arrange_scales -- the scales of quantised K^ and V^T re-ordered, per kv
+ * tile of mxattn_kv_tile() keys, into the order in which the attention kernel's
+ * lanes hand them to its block-scaled MFMAs (mxattn_forward does this in its own
+ * workspace).  For callers that quantise K and V once and attend to them many
+ * times (cached keys and values, query chunks): arrange once, then call
+ * mxattn_forward_arranged, whose kernel then needs no per-tile byte gathers.
+ *   Ks  [B, H, Nkv, d/32] (AXIS_LAST), VTs [B, H, d, P/32] (AXIS_ROWS),
+ *   P = mxattn_padded_tokens(Nkv).
+ *   Ksa, VTsa: B*H*P*4 bytes each, 16-byte aligned, owned by the caller; per head
+ *   and kv tile j, 512 bytes each.  With lane = 0..63, i = lane % 32, g = lane / 32
+ *   and kappa(t, r) = 64(t/2) + 32((r/4)%2) + 16(t%2) + 4(r/8) + r%4:
+ *     Ksa  dword 2 lane + s, byte t (t < 4): the Ks byte of key 128 j + kappa(t, i),
+ *          block 2s + g, for s < d/64 (0 for keys past Nkv, and in dwords s >= d/64);
+ *     VTsa dword 2 lane + c, byte ct: the VTs byte of channel 32 ct + i, block
+ *          4 j + 2c + g, for ct < d/32 (bytes ct >= d/32 are 0).
+ *   d must be 64 or 128; 1 <= Nkv <= 2^24.
+ */
+int mxattn_arrange_scales(const uint8_t* Ks, const uint8_t* VTs, int64_t B, int64_t H, int64_t Nkv, int64_t d,
+                          uint8_t* Ksa, uint8_t* VTsa, void* stream);
+
+/*
+ * mxattn_forward_arranged -- mxattn_forward_quantized without the P^ dump, on K^ and
+ * V^T scales in the order mxattn_arrange_scales writes (Qc, Qs, Kc, VTc as for
+ * mxattn_forward_quantized).  This is the attention kernel mxattn_forward runs
+ * after its quantisation passes; the output is bitwise that of
+ * mxattn_forward_quantized on the same operands.
+ */
+int mxattn_forward_arranged(const uint8_t* Qc, const uint8_t* Qs,
+                            const uint8_t* Kc, const uint8_t* Ksa,
+                            const uint8_t* VTc, const uint8_t* VTsa,
+                            int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
+                            float softmax_scale, uint32_t pnq,
+                            int32_t p_rule_kind, float p_qmax,
+                            void* O, int32_t out_dtype, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* mxattn_last_error(void);

@@ -7,7 +7,8 @@ built first (``python mxfp4_bit_attention_amd/build.py``); importing this
 module raises if it is missing, and nothing here falls back to a CPU path.
 
 Names mirror the C entry points: ``mxattn_quantize``, ``mxattn_quant_error``, ``mxattn_forward``,
-``mxattn_forward_quantized``, ``mxattn_forward_workspace_bytes``,
+``mxattn_forward_quantized``, ``mxattn_arrange_scales``, ``mxattn_forward_arranged``,
+``mxattn_forward_workspace_bytes``,
 ``mxattn_kv_tile``, ``mxattn_padded_tokens``, ``mxattn_last_error``.
 Rules are given as ``"uos"``, ``"ocp"`` or ``("ceil", q)``.
 """
@@ -31,6 +32,7 @@ MXATTN_AXIS_LAST, MXATTN_AXIS_ROWS = 0, 1
 EXPORTED = (
     "mxattn_kv_tile", "mxattn_padded_tokens", "mxattn_quantize", "mxattn_forward_workspace_bytes",
     "mxattn_forward", "mxattn_forward_quantized", "mxattn_last_error", "mxattn_quant_error",
+    "mxattn_arrange_scales", "mxattn_forward_arranged",
 )
 
 
@@ -64,6 +66,11 @@ def _load() -> ctypes.CDLL:
     lib.mxattn_forward_quantized.restype = c.c_int
     lib.mxattn_forward_quantized.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, u32,
                                              i32, f32, vp, i32, vp, vp, vp]
+    lib.mxattn_arrange_scales.restype = c.c_int
+    lib.mxattn_arrange_scales.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.mxattn_forward_arranged.restype = c.c_int
+    lib.mxattn_forward_arranged.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, u32, i32, f32,
+                                            vp, i32, vp]
     return lib
 
 
@@ -252,4 +259,40 @@ def mxattn_forward_quantized(qc, qs, kc, ks, vtc, vts, Nkv: int, softmax_scale: 
                                         _stream(qc.device)))
     if dump_p:
         return out, pc, ps
+    return out
+
+
+def mxattn_arrange_scales(ks, vts, Nkv: int):
+    """ks [B,H,Nkv,d/32], vts [B,H,d,P/32] -> (ksa, vtsa), uint8 [B,H,P*4] each, in the
+    per-kv-tile order of the attention kernel's MFMA scale operands."""
+    torch = _torch()
+    _need_cuda(ks, vts)
+    B, H, nk, dg = ks.shape
+    d = dg * 32
+    P = mxattn_padded_tokens(Nkv)
+    if nk != Nkv or tuple(vts.shape) != (B, H, d, P // 32):
+        raise ValueError("ks must be [B, H, Nkv, d/32] and vts [B, H, d, P/32]")
+    ksa = torch.empty((B, H, P * 4), dtype=torch.uint8, device=ks.device)
+    vtsa = torch.empty((B, H, P * 4), dtype=torch.uint8, device=ks.device)
+    _check(LIB.mxattn_arrange_scales(_ptr(ks), _ptr(vts), B, H, Nkv, d, _ptr(ksa), _ptr(vtsa),
+                                     _stream(ks.device)))
+    return ksa, vtsa
+
+
+def mxattn_forward_arranged(qc, qs, kc, ksa, vtc, vtsa, Nkv: int, softmax_scale: float, pnq: bool = True,
+                            p_rule="uos", out_dtype=None, out=None):
+    """mxattn_forward_quantized on scales from mxattn_arrange_scales (no P^ dump)."""
+    torch = _torch()
+    _need_cuda(qc, qs, kc, ksa, vtc, vtsa)
+    B, H, Nq, dh = qc.shape
+    d = dh * 2
+    if out_dtype is None:
+        out_dtype = torch.float32
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=qc.device)
+    _need_cuda(out)
+    kind, qm = rule_args(p_rule)
+    _check(LIB.mxattn_forward_arranged(_ptr(qc), _ptr(qs), _ptr(kc), _ptr(ksa), _ptr(vtc), _ptr(vtsa),
+                                       B, H, Nq, Nkv, d, float(softmax_scale), int(bool(pnq)), kind, qm,
+                                       _ptr(out), _dtype_code(out), _stream(qc.device)))
     return out

@@ -95,10 +95,11 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t kc, ks, vc, vs, total;
+  size_t kc, ks, vc, vs, ksa, vsa, total;
 };
 
-// The forward's workspace: K^ and V^T (Q is quantised inside the attention kernel).
+// The forward's workspace: K^ and V^T (Q is quantised inside the attention kernel),
+// and both scale sets re-ordered per kv tile for the attention kernel's lanes.
 bool fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, FwdLayout* L) {
   int64_t nq_e, nkv_e, v_e;
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
@@ -108,6 +109,8 @@ bool fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, FwdLay
   L->ks = c.take((size_t)nkv_e / 32);
   L->vc = c.take((size_t)v_e / 2);
   L->vs = c.take((size_t)v_e / 32);
+  L->ksa = c.take((size_t)(B * H * P) * 4);
+  L->vsa = c.take((size_t)(B * H * P) * 4);
   L->total = c.off;
   return true;
 }
@@ -231,7 +234,8 @@ static int attention_core(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* K
                           const uint8_t* VTc, const uint8_t* VTs, int64_t B, int64_t H, int64_t Nq,
                           int64_t Nkv, int64_t d, float softmax_scale, uint32_t pnq,
                           const mxattn::Rule& pr, void* O, int32_t out_dtype, uint8_t* pc, uint8_t* ps,
-                          hipStream_t s, const char* who, const QuantQ* fused = nullptr) {
+                          hipStream_t s, const char* who, const QuantQ* fused = nullptr,
+                          const uint8_t* ksa = nullptr, const uint8_t* vsa = nullptr) {
   mxattn::AttnArgs a{};
   a.qc = Qc;
   a.qs = Qs;
@@ -239,6 +243,8 @@ static int attention_core(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* K
   a.ks = Ks;
   a.vc = VTc;
   a.vs = VTs;
+  a.ksa = ksa;
+  a.vsa = vsa;
   a.o = O;
   a.pc = pc;
   a.ps = ps;
@@ -279,6 +285,36 @@ int mxattn_forward_quantized(const uint8_t* Qc, const uint8_t* Qs, const uint8_t
                         p_codes, p_scales, static_cast<hipStream_t>(stream), who);
 }
 
+int mxattn_arrange_scales(const uint8_t* Ks, const uint8_t* VTs, int64_t B, int64_t H, int64_t Nkv, int64_t d,
+                          uint8_t* Ksa, uint8_t* VTsa, void* stream) {
+  const char* who = "mxattn_arrange_scales";
+  if (!Ks || !VTs || !Ksa || !VTsa) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if (!aligned16(Ks) || !aligned16(VTs) || !aligned16(Ksa) || !aligned16(VTsa))
+    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if (int st = check_attn_shape(B, H, 1, Nkv, d, 1.0f, who)) return st;
+  hipError_t e = mxattn::launch_arrange_scales(Ks, VTs, B * H, Nkv, round_up(Nkv, mxattn::kKvTile), (int)d, Ksa,
+                                               VTsa, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, who);
+  return ok();
+}
+
+int mxattn_forward_arranged(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* Kc, const uint8_t* Ksa,
+                            const uint8_t* VTc, const uint8_t* VTsa, int64_t B, int64_t H, int64_t Nq,
+                            int64_t Nkv, int64_t d, float softmax_scale, uint32_t pnq, int32_t p_rule_kind,
+                            float p_qmax, void* O, int32_t out_dtype, void* stream) {
+  const char* who = "mxattn_forward_arranged";
+  if (!Qc || !Qs || !Kc || !Ksa || !VTc || !VTsa || !O) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if (!aligned16(Qc) || !aligned16(Qs) || !aligned16(Kc) || !aligned16(Ksa) || !aligned16(VTc) ||
+      !aligned16(VTsa) || !aligned16(O))
+    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if (!elem_bytes(out_dtype)) return fail(MXATTN_E_INVALID, "%s: out_dtype must be MXATTN_F32 or MXATTN_BF16", who);
+  if (int st = check_attn_shape(B, H, Nq, Nkv, d, softmax_scale, who)) return st;
+  mxattn::Rule pr{};
+  if (int st = make_rule(p_rule_kind, p_qmax, &pr, who)) return st;
+  return attention_core(Qc, Qs, Kc, nullptr, VTc, nullptr, B, H, Nq, Nkv, d, softmax_scale, pnq, pr, O, out_dtype,
+                        nullptr, nullptr, static_cast<hipStream_t>(stream), who, nullptr, Ksa, VTsa);
+}
+
 int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, int64_t B, int64_t H,
                    int64_t Nq, int64_t Nkv, int64_t d, float softmax_scale, uint32_t hadamard,
                    uint32_t pnq, int32_t rule_kind, float qmax, void* O, void* workspace,
@@ -299,7 +335,7 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, i
   if (workspace_bytes < L.total)
     return fail(MXATTN_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, workspace_bytes, L.total);
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  uint8_t *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs;
+  uint8_t *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs, *ksa = w + L.ksa, *vsa = w + L.vsa;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
   const float c = inv_sqrt_f32((int)d);
@@ -309,11 +345,12 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, i
   else
     e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, nullptr, s);
   if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vs, rule, nullptr, s);
+  if (e == hipSuccess) e = mxattn::launch_arrange_scales(ks, vs, B * H, Nkv, P, (int)d, ksa, vsa, s);
   if (e != hipSuccess) return hip_fail(e, who);
   // Q is read once per query tile: the attention kernel rotates and quantises it itself
   const QuantQ fused{Q, eb == 2, hadamard != 0, c};
   return attention_core(nullptr, nullptr, kc, ks, vc, vs, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O, dtype,
-                        nullptr, nullptr, s, who, &fused);
+                        nullptr, nullptr, s, who, &fused, ksa, vsa);
 }
 
 }  // extern "C"

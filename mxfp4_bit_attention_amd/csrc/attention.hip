@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "launch.h"
@@ -81,6 +82,11 @@ constexpr int BR = 32 * NW;  // queries per workgroup
 //  K scales [4 i + t] dwords: the d/32 scale bytes of key kappa(t, i)
 //  V codes  [ct][c][l]: unit (ct, c, l) = keys 64c + 32(l/32) .. +31 of channel 32ct + l%32
 //  V scales [NCT i + ct] dwords: the 4 scale bytes (one per 32-key block) of channel 32ct + i
+// or, when the scales come pre-arranged (the forward's own workspace, written by
+// k_arrange_scales), the two scale regions hold exactly the lanes' MFMA scale operands:
+//  K scales [2 lane + s] dwords: byte t = scale of key kappa(t, lane%32), d-block 2s + lane/32
+//  V scales [2 lane + c] dwords: byte ct = scale of channel 32ct + lane%32, key block 2c + lane/32
+// so a lane loads its operands with one 8-byte read and no byte gathers.
 template <int D>
 struct Geo {
   static constexpr int S = D / 64;     // d-steps of an S^T MFMA
@@ -88,7 +94,7 @@ struct Geo {
   static constexpr int KC = BC * D / 2;
   static constexpr int KS = 4 * BC;
   static constexpr int VC = D * BC / 2;
-  static constexpr int VS = 4 * D;
+  static constexpr int VS = 4 * BC;  // the larger of 4 D (gathered) and 512 (pre-arranged)
   static constexpr int OFF_KS = KC;
   static constexpr int OFF_VC = KC + KS;
   static constexpr int OFF_VS = KC + KS + VC;
@@ -112,7 +118,7 @@ struct DmaOffsets {
   uint32_t s;  // waves 0-1: key scales; waves 2-3: channel scales
 };
 
-template <int D>
+template <int D, bool PRE>
 __device__ __forceinline__ DmaOffsets<D> dma_offsets(int64_t kv_pad, int wave, int lane) {
   using G = Geo<D>;
   DmaOffsets<D> o;
@@ -128,7 +134,9 @@ __device__ __forceinline__ DmaOffsets<D> dma_offsets(int64_t kv_pad, int wave, i
     const int ct = p / 128, c = (p / 64) % 2, l = p % 64;
     o.v[u] = (uint32_t)((32 * ct + (l & 31)) * (kv_pad / 2) + 32 * c + 16 * (l >> 5));
   }
-  if (wave < 2) {
+  if constexpr (PRE) {
+    o.s = (uint32_t)(4 * (64 * (wave & 1) + lane));  // 512 contiguous bytes per tile, K or V
+  } else if (wave < 2) {
     const int p = 64 * wave + lane;  // dword 4 i + t of the K scale region
     o.s = (uint32_t)(kappa(p % 4, p / 4) * (D / 32));
   } else {
@@ -159,7 +167,7 @@ struct TileSrc {
 // left), so keys past the last one, and whole tiles past the end, read as zero
 // without touching memory.  Past the end the V^ descriptors still cover the head's
 // other channels: those reads stay inside the head's V^ and are never used.
-template <int D>
+template <int D, bool PRE>
 __device__ __forceinline__ void tile_dma(uint8_t* st, const DmaOffsets<D>& o, const TileSrc& src, int j, int wave,
                                          int lane) {
   using G = Geo<D>;
@@ -170,7 +178,11 @@ __device__ __forceinline__ void tile_dma(uint8_t* st, const DmaOffsets<D>& o, co
   for (int u = 0; u < G::CODE_DMA; ++u) dma16(rk, st + 1024 * (G::CODE_DMA * wave + u), o.k[u]);
 #pragma unroll
   for (int u = 0; u < G::CODE_DMA; ++u) dma16(rv, st + G::OFF_VC + 1024 * (G::CODE_DMA * wave + u), o.v[u]);
-  if (wave < 2) {
+  if constexpr (PRE) {
+    const int so = 512 * j;
+    if (wave < 2) dma4(rsrc(src.ks + so, max(src.ks_bytes - so, 0)), st + G::OFF_KS + 256 * wave, o.s);
+    else dma4(rsrc(src.vs + so, max(src.vs_bytes - so, 0)), st + G::OFF_VS + 256 * (wave - 2), o.s);
+  } else if (wave < 2) {
     const __amdgpu_buffer_rsrc_t rs = rsrc(src.ks + ks0, max(src.ks_bytes - ks0, 0));
     // a key's scales are one dword at D = 128, two bytes at D = 64
     if constexpr (D == 128) dma4(rs, st + G::OFF_KS + 256 * wave, o.s);
@@ -217,8 +229,13 @@ __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
   return fmaxf(fmax3(w0, w1, w2), w3);
 }
 
-// Make the compiler produce these values at this point of the program.
-__device__ __forceinline__ void pin(v16f (&x)[4]) { asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])); }
+// Make the compiler produce these values at this point of the program (and not sink
+// the instructions that produce them into a later branch).
+template <int N>
+__device__ __forceinline__ void pin_all(v16f (&x)[N], float& l) {
+  if constexpr (N == 4) asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(l));
+  else asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(l));
+}
 
 // Interleave the next N MFMAs of the scheduling region with K ALU/transcendental
 // instructions each.
@@ -269,7 +286,7 @@ __device__ __forceinline__ void pv_mfma(v16f (&acc)[D / 32], v16f& rs, const v8i
 
 // One kv tile for one wave's 32 queries.  `rem` (TAIL only) is the number of valid
 // keys in the tile.
-template <int D, bool PNQ, bool DUMP, bool TAIL>
+template <int D, bool PRE, bool PNQ, bool DUMP, bool TAIL>
 __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int lane, Sel sel0, Sel sel1, int rem,
                                             const v8i (&qf)[D / 64], const int (&qsc)[D / 64],
                                             v16f (&acc)[D / 32], float& m, float& l, float cl, Rule prule,
@@ -291,7 +308,11 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
       kf[t][s] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
   int ksw[S];
-  {
+  if constexpr (PRE) {
+    const u32x2 d = *reinterpret_cast<const u32x2*>(st + G::OFF_KS + 8 * lane);
+    ksw[0] = (int)d.x;
+    if constexpr (S == 2) ksw[1] = (int)d.y;
+  } else {
     const u32x4 d = *reinterpret_cast<const u32x4*>(st + G::OFF_KS + 16 * i);
     ksw[0] = (int)gather4(d, sel0);
     if constexpr (S == 2) ksw[1] = (int)gather4(d, sel1);
@@ -343,7 +364,11 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
       vf[ct][c] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
     }
   int vsw[2];
-  if constexpr (NCT == 4) {
+  if constexpr (PRE) {
+    const u32x2 d = *reinterpret_cast<const u32x2*>(st + G::OFF_VS + 8 * lane);
+    vsw[0] = (int)d.x;
+    vsw[1] = (int)d.y;
+  } else if constexpr (NCT == 4) {
     const u32x4 d = *reinterpret_cast<const u32x4*>(st + G::OFF_VS + 16 * i);
     vsw[0] = (int)gather4(d, sel0);
     vsw[1] = (int)gather4(d, sel1);
@@ -481,7 +506,7 @@ __device__ __forceinline__ void quantise_q_blocks(const AttnArgs& a, int64_t row
 }
 
 // One workgroup = NW waves of 32 queries.
-template <int D, bool PNQ, bool DUMP>
+template <int D, bool PRE, bool PNQ, bool DUMP>
 __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   using G = Geo<D>;
   constexpr int S = G::S;
@@ -514,9 +539,13 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
   const uint8_t* qc = a.qc + head * a.nq * (D / 2);
   const uint8_t* qs = a.qs + head * a.nq * (D / 32);
   const int kvp = (int)a.kv_pad;
-  const TileSrc src{a.kc + head * a.nkv * (D / 2), a.ks + head * a.nkv * (D / 32),
-                    a.vc + head * (int64_t)D * (kvp / 2), a.vs + head * (int64_t)D * (kvp / 32),
-                    nkv * (D / 2), nkv * (D / 32), D * (kvp / 2), D * (kvp / 32)};
+  const int arr = 4 * kvp;  // bytes of one head's pre-arranged K (or V) scales: 512 per tile
+  const TileSrc src = PRE ? TileSrc{a.kc + head * a.nkv * (D / 2), a.ksa + head * arr,
+                                    a.vc + head * (int64_t)D * (kvp / 2), a.vsa + head * arr,
+                                    nkv * (D / 2), arr, D * (kvp / 2), arr}
+                          : TileSrc{a.kc + head * a.nkv * (D / 2), a.ks + head * a.nkv * (D / 32),
+                                    a.vc + head * (int64_t)D * (kvp / 2), a.vs + head * (int64_t)D * (kvp / 32),
+                                    nkv * (D / 2), nkv * (D / 32), D * (kvp / 2), D * (kvp / 32)};
 
   // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop: lane (i, h) holds
   // blocks 2s + h of query row i.  Either read from the quantised Q^, or made here
@@ -556,9 +585,9 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
 
   // ---- three-stage ring: tile j lives in stage j % 3; its DMA is issued two tiles
   // ahead, right after the barrier that retires the reads of the stage it reuses.
-  const DmaOffsets<D> dof = dma_offsets<D>(a.kv_pad, wave, lane);
-  tile_dma<D>(st0, dof, src, 0, wave, lane);
-  tile_dma<D>(st1, dof, src, 1, wave, lane);
+  const DmaOffsets<D> dof = dma_offsets<D, PRE>(a.kv_pad, wave, lane);
+  tile_dma<D, PRE>(st0, dof, src, 0, wave, lane);
+  tile_dma<D, PRE>(st1, dof, src, 1, wave, lane);
   if (tid < 4) lones[tid] = 0x22222222u;
 
   // Wait for this wave's DMAs of tile j (those of tile j + 1 may stay in flight);
@@ -573,22 +602,26 @@ __global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtil
     stage_barrier();
     uint8_t* cur = sj == 0 ? st0 : (sj == 1 ? st1 : st2);
     uint8_t* nxt = sj == 0 ? st2 : (sj == 1 ? st0 : st1);
-    tile_dma<D>(nxt, dof, src, j + 2, wave, lane);
+    tile_dma<D, PRE>(nxt, dof, src, j + 2, wave, lane);
     sj = sj == 2 ? 0 : sj + 1;
     return cur;
   };
   int j = 0;
   for (; j < nfull; ++j) {
     const uint8_t* cur = enter(j);
-    attend_tile<D, PNQ, DUMP, false>(cur, lane, sel0, sel1, BC, qf, qsc, acc, m, l, cl, prule, a, qrow, head, j,
+    attend_tile<D, PRE, PNQ, DUMP, false>(cur, lane, sel0, sel1, BC, qf, qsc, acc, m, l, cl, prule, a, qrow, head, j,
                                      lones);
   }
   if (j < ntiles) {  // the ragged last tile, masked
     const uint8_t* cur = enter(j);
-    attend_tile<D, PNQ, DUMP, true>(cur, lane, sel0, sel1, nkv - j * BC, qf, qsc, acc, m, l, cl, prule, a, qrow,
+    attend_tile<D, PRE, PNQ, DUMP, true>(cur, lane, sel0, sel1, nkv - j * BC, qf, qsc, acc, m, l, cl, prule, a, qrow,
                                     head, j, lones);
   }
   MX_VMCNT(0);  // no DMA may still target this workgroup's LDS when it exits
+  // Keep the last tile's MFMAs out of the epilogue's divergent branch below: an MFMA
+  // reads its operands across the whole wave, so under a partial exec mask (a wave
+  // holding query rows past the end) it would drop the inactive lanes' channels.
+  pin_all(acc, l);
 
   // ---- epilogue: O = O~ / l
   if (qrow < a.nq) {
@@ -622,14 +655,71 @@ static hipError_t launch_d(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) {
   const int nblocks = (int)nb;
   const unsigned grid = (unsigned)((nblocks + 7) / 8 * 8);
   const bool dump = a.pc != nullptr;
-  if (pnq && !dump)
-    hipLaunchKernelGGL((k_attn<D, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  const bool pre = a.ksa != nullptr;
+  if (pre && dump) return hipErrorInvalidValue;  // the P^ dump comes with caller-layout operands only
+  if (pre && pnq)
+    hipLaunchKernelGGL((k_attn<D, true, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  else if (pre)
+    hipLaunchKernelGGL((k_attn<D, true, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  else if (pnq && !dump)
+    hipLaunchKernelGGL((k_attn<D, false, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else if (pnq && dump)
-    hipLaunchKernelGGL((k_attn<D, true, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, false, true, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else if (!dump)
-    hipLaunchKernelGGL((k_attn<D, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, false, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
   else
-    hipLaunchKernelGGL((k_attn<D, false, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+    hipLaunchKernelGGL((k_attn<D, false, false, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  return hipGetLastError();
+}
+
+// Pre-arranged scales (the layouts described with Geo): one thread per output dword,
+// K dwords first, then V.  Keys past the last one get scale byte 0.
+template <int D>
+__global__ void k_arrange_scales(const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vs, int64_t heads,
+                                 int nkv, int kv_pad, uint32_t* __restrict__ ksa, uint32_t* __restrict__ vsa) {
+  const int64_t per_head = (int64_t)kv_pad;  // dwords per head in each layout: 128 per tile
+  const int64_t total = heads * per_head;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < 2 * total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const bool isv = idx >= total;
+    const int64_t r = isv ? idx - total : idx;
+    const int64_t head = r / per_head;
+    const int q = (int)(r % per_head);
+    const int j = q >> 7, lane = (q & 127) >> 1, sc = q & 1;
+    const int i = lane & 31, h = lane >> 5;
+    uint32_t w = 0;
+    if (!isv) {
+      if (sc < D / 64) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int key = BC * j + kappa(t, i);
+          if (key < nkv) w |= (uint32_t)ks[(head * nkv + key) * (D / 32) + 2 * sc + h] << (8 * t);
+        }
+      }
+      ksa[r] = w;
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < D / 32; ++ct)
+        w |= (uint32_t)vs[(head * D + 32 * ct + i) * (kv_pad / 32) + 4 * j + 2 * sc + h] << (8 * ct);
+      vsa[r] = w;
+    }
+  }
+}
+
+hipError_t launch_arrange_scales(const uint8_t* ks, const uint8_t* vs, int64_t heads, int64_t nkv, int64_t kv_pad,
+                                 int d, uint8_t* ksa, uint8_t* vsa, hipStream_t s) {
+  const int64_t n = 2 * heads * kv_pad;
+  const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, 256 * 16);
+  uint32_t* ka = reinterpret_cast<uint32_t*>(ksa);
+  uint32_t* va = reinterpret_cast<uint32_t*>(vsa);
+  if (d == 128)
+    hipLaunchKernelGGL((k_arrange_scales<128>), dim3(grid), dim3(256), 0, s, ks, vs, heads, (int)nkv, (int)kv_pad, ka,
+                       va);
+  else if (d == 64)
+    hipLaunchKernelGGL((k_arrange_scales<64>), dim3(grid), dim3(256), 0, s, ks, vs, heads, (int)nkv, (int)kv_pad, ka,
+                       va);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

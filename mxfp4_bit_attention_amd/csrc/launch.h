@@ -37,6 +37,10 @@ struct AttnArgs {
   const uint8_t* ks;
   const uint8_t* vc;
   const uint8_t* vs;
+  // Optional pre-arranged K^ and V^T scales (launch_arrange_scales); when set, ks and
+  // vs are unused.  512 bytes per kv tile per head, each.
+  const uint8_t* ksa;
+  const uint8_t* vsa;
   void* o;
   uint8_t* pc;   // optional P^ dump
   uint8_t* ps;
@@ -55,6 +59,10 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, int d, int pnq, Rule p_rule, hipStream_t s);
+// Re-orders the scales of K^ [heads, nkv, d/32] and V^T [heads, d, kv_pad/32] into the
+// per-tile order the attention kernel's lanes use (heads * kv_pad * 4 bytes each).
+hipError_t launch_arrange_scales(const uint8_t* ks, const uint8_t* vs, int64_t heads, int64_t nkv, int64_t kv_pad,
+                                 int d, uint8_t* ksa, uint8_t* vsa, hipStream_t s);
 
 constexpr int kKvTile = 128;
 

@@ -74,6 +74,18 @@ int main(void) {
                                   MXATTN_RULE_OCP, 0.f, FAKE, 5, NULL, NULL, NULL),
          MXATTN_E_INVALID, "forward_quantized out dtype");
 
+  expect(mxattn_arrange_scales(FAKE8, FAKE8, 1, 2, 300, 128, NULL, FAKE8, NULL), MXATTN_E_INVALID,
+         "arrange null output");
+  expect(mxattn_arrange_scales(FAKE8, (const uint8_t*)MIS, 1, 2, 300, 128, FAKE8, FAKE8, NULL), MXATTN_E_INVALID,
+         "arrange misaligned");
+  expect(mxattn_arrange_scales(FAKE8, FAKE8, 1, 2, 300, 80, FAKE8, FAKE8, NULL), MXATTN_E_UNSUPPORTED,
+         "arrange d");
+  expect(mxattn_forward_arranged(FAKE8, FAKE8, FAKE8, NULL, FAKE8, FAKE8, 1, 2, 256, 256, 64, 0.125f, 1,
+                                 MXATTN_RULE_UOS, 0.f, FAKE, MXATTN_F32, NULL), MXATTN_E_INVALID,
+         "forward_arranged null scales");
+  expect(mxattn_forward_arranged(FAKE8, FAKE8, FAKE8, FAKE8, FAKE8, FAKE8, 1, 2, 256, 256, 64, 0.125f, 1, 9, 0.f,
+                                 FAKE, MXATTN_F32, NULL), MXATTN_E_INVALID, "forward_arranged rule");
+
   /* a long message must not overflow the thread-local buffer */
   for (int i = 0; i < 1000; ++i)
     (void)mxattn_quantize(FAKE, 1000 + i, 1, 32, 128, 0, 0, 0.f, 0, FAKE8, FAKE8, NULL);

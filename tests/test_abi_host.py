@@ -51,6 +51,7 @@ def test_constants(mx):
     ws = mx.mxattn_forward_workspace_bytes(1, 40, 75600, 75600, 128)
     n = 40 * 75600 * 128
     assert ws >= n // 2 + n // 32 + 40 * 128 * 75648 // 2 + 40 * 128 * 75648 // 32  # K^ and V^T
+    assert ws >= n // 2 + n // 32 + 40 * 128 * 75648 * 17 // 32 + 2 * 40 * 75648 * 4  # + arranged scales
     assert ws % 256 == 0
     assert mx.mxattn_forward_workspace_bytes(1, 1, 1, 1, 96) == 0
     assert mx.mxattn_forward_workspace_bytes(0, 1, 1, 1, 64) == 0
@@ -143,6 +144,51 @@ def test_forward_quantized_rejects_bad_arguments(mx):
     bad = list(args)
     bad[10] = 32
     assert L.mxattn_forward_quantized(*bad) == -2
+
+
+def test_arrange_scales_rejects_bad_arguments(mx):
+    p = ctypes.c_void_p
+    L = mx.LIB
+    args = [p(FAKE), p(FAKE), 1, 2, 300, 128, p(FAKE), p(FAKE), None]
+    bad = list(args)
+    bad[6] = None
+    assert L.mxattn_arrange_scales(*bad) == -1 and "null" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[1] = p(MISALIGNED)
+    assert L.mxattn_arrange_scales(*bad) == -1 and "aligned" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[5] = 96
+    assert L.mxattn_arrange_scales(*bad) == -2
+    bad = list(args)
+    bad[4] = 0
+    assert L.mxattn_arrange_scales(*bad) == -1 and ">= 1" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[4] = (1 << 24) + 1
+    assert L.mxattn_arrange_scales(*bad) == -1 and "tokens per head" in mx.mxattn_last_error()
+
+
+def test_forward_arranged_rejects_bad_arguments(mx):
+    p = ctypes.c_void_p
+    L = mx.LIB
+    args = [p(FAKE)] * 6 + [1, 1, 16, 16, 128, 0.1, 1, 0, 0.0, p(FAKE), 1, None]
+    bad = list(args)
+    bad[3] = None
+    assert L.mxattn_forward_arranged(*bad) == -1 and "null" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[5] = p(MISALIGNED)
+    assert L.mxattn_forward_arranged(*bad) == -1 and "aligned" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[16] = 3
+    assert L.mxattn_forward_arranged(*bad) == -1 and "out_dtype" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[10] = 32
+    assert L.mxattn_forward_arranged(*bad) == -2
+    bad = list(args)
+    bad[11] = -1.0
+    assert L.mxattn_forward_arranged(*bad) == -1 and "softmax_scale" in mx.mxattn_last_error()
+    bad = list(args)
+    bad[13] = 7
+    assert L.mxattn_forward_arranged(*bad) == -1 and "rule" in mx.mxattn_last_error()
 
 
 def test_binding_rule_parsing(mx):

@@ -235,3 +235,69 @@ def test_fused_q_quantisation_is_bitwise_the_quantiser(dtype, d, had, rule):
     torch.cuda.synchronize()
     iv = torch.int16 if O.dtype == torch.bfloat16 else torch.int32
     assert torch.equal(O.view(iv), O2.view(iv))
+
+
+def _arranged_reference(ks, vts, Nkv, d):
+    """The order mxattn_arrange_scales documents, written out on the host: per head and
+    kv tile j, dword 2 lane + s byte t of K = key 128 j + kappa(t, lane % 32), block
+    2s + lane // 32; dword 2 lane + c byte ct of V = channel 32 ct + lane % 32, block
+    4 j + 2c + lane // 32."""
+    B, H = ks.shape[:2]
+    ntiles = vts.shape[-1] // 4
+    ka = np.zeros((B, H, ntiles, 64, 2, 4), np.uint8)
+    va = np.zeros((B, H, ntiles, 64, 2, 4), np.uint8)
+    tiles = np.arange(ntiles)
+    for lane in range(64):
+        i, g = lane % 32, lane // 32
+        for t in range(4):
+            kap = 64 * (t // 2) + 32 * ((i // 4) % 2) + 16 * (t % 2) + 4 * (i // 8) + i % 4
+            keys = 128 * tiles + kap
+            ok = keys < Nkv
+            for s in range(d // 64):
+                ka[:, :, ok, lane, s, t] = ks[:, :, keys[ok], 2 * s + g]
+        for c in range(2):
+            for ct in range(d // 32):
+                va[:, :, :, lane, c, ct] = vts[:, :, 32 * ct + i, 4 * tiles + 2 * c + g]
+    return ka.reshape(B, H, -1), va.reshape(B, H, -1)
+
+
+def _device_operands(B, H, Nq, Nkv, d, seed):
+    torch, mx = require_gpu()
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn((B, H, Nq, d), generator=g, device="cuda") * 1.5
+    k = torch.randn((B, H, Nkv, d), generator=g, device="cuda") * 1.5
+    v = torch.randn((B, H, Nkv, d), generator=g, device="cuda")
+    qc, qs = mx.mxattn_quantize(q.view(-1, Nq, d), rule="uos", axis="last", hadamard=True)
+    kc, ks = mx.mxattn_quantize(k.view(-1, Nkv, d), rule="uos", axis="last", hadamard=True)
+    vc, vs = mx.mxattn_quantize(v.view(-1, Nkv, d), rule="uos", axis="rows")
+    sh = lambda t: t.view(B, H, *t.shape[1:])
+    return tuple(map(sh, (qc, qs, kc, ks, vc, vs)))
+
+
+@pytest.mark.parametrize("B,H,Nkv,d", [(1, 1, 1, 64), (2, 3, 300, 128), (1, 2, 1000, 64), (1, 1, 4096, 128)])
+def test_arranged_scales_follow_the_documented_order(B, H, Nkv, d):
+    torch, mx = require_gpu()
+    qc, qs, kc, ks, vc, vs = _device_operands(B, H, 4, Nkv, d, seed=Nkv + d)
+    ksa, vsa = mx.mxattn_arrange_scales(ks, vs, Nkv)
+    torch.cuda.synchronize()
+    ka, va = _arranged_reference(ks.cpu().numpy(), vs.cpu().numpy(), Nkv, d)
+    assert np.array_equal(ksa.cpu().numpy(), ka)
+    assert np.array_equal(vsa.cpu().numpy(), va)
+
+
+@pytest.mark.parametrize("pnq", [True, False])
+@pytest.mark.parametrize("B,H,Nq,Nkv,d", [(1, 1, 300, 1000, 128), (2, 2, 64, 33, 64), (1, 1, 1, 129, 64),
+                                          (1, 3, 517, 1, 128), (1, 2, 2048, 4096, 128)])
+def test_arranged_entry_is_bitwise_the_quantized_entry(B, H, Nq, Nkv, d, pnq):
+    """mxattn_forward_arranged runs the kernel variant mxattn_forward uses (scale operands
+    loaded directly); on the same operands it must give exactly the caller-layout entry's O."""
+    torch, mx = require_gpu()
+    qc, qs, kc, ks, vc, vs = _device_operands(B, H, Nq, Nkv, d, seed=Nq * 7 + Nkv + d)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    ksa, vsa = mx.mxattn_arrange_scales(ks, vs, Nkv)
+    for rule in ("uos", "ocp"):
+        o1 = mx.mxattn_forward_quantized(qc, qs, kc, ks, vc, vs, Nkv, scale, pnq=pnq, p_rule=rule)
+        o2 = mx.mxattn_forward_arranged(qc, qs, kc, ksa, vc, vsa, Nkv, scale, pnq=pnq, p_rule=rule)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o1).all()
+        assert torch.equal(o1, o2), rule
