@@ -24,6 +24,9 @@
 // the P^ V product uses.  A 32x32x64 MFMA leaves the vector ALU free for part of
 // its duration (the 16x16x128 form does not), so ALU work placed beside these
 // MFMAs, in this wave or in the other wave of the SIMD, runs in their shadow.
+// The MFMAs' E8M0 scale operands come either pre-arranged per tile in the lanes'
+// operand order (k_arrange_scales; one 8-byte LDS read per lane and tile) or in the
+// quantiser's layout, from which each lane gathers its bytes with v_perm.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
