@@ -23,7 +23,7 @@
 // extra MFMA per chunk against an all-ones A operand, which sums the same P^ codes
 // the P^ V product uses.  A 32x32x64 MFMA leaves the vector ALU free for part of
 // its duration (the 16x16x128 form does not), so ALU work placed beside these
-// MFMAs, in this wave or in the other wave of the SIMD, runs in their shadow.
+// MFMAs, in this wave or in the other waves of the SIMD, runs in their shadow.
 // The MFMAs' E8M0 scale operands come either pre-arranged per tile in the lanes'
 // operand order (k_arrange_scales; one 8-byte LDS read per lane and tile) or in the
 // quantiser's layout, from which each lane gathers its bytes with v_perm.
@@ -66,10 +66,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 }
 
 constexpr int BC = kKvTile;  // 128 keys per kv tile
-// A workgroup is 4 waves (one per SIMD) of 32 queries each, and two workgroups share
-// a CU: each SIMD then runs one wave of each, and since the workgroups synchronise on
-// separate barriers they drift out of phase, so one wave's softmax runs beside the
-// other's MFMAs.
+// A workgroup is 4 waves (one per SIMD) of 32 queries each, and three workgroups share
+// a CU (at most 168 VGPRs per wave, 3 x 52 KB of LDS): each SIMD then runs one wave of
+// each, and since the workgroups synchronise on separate barriers they drift out of
+// phase, so one wave's softmax runs beside another's MFMAs.
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;  // threads per workgroup
 constexpr int BR = 32 * NW;  // queries per workgroup
@@ -272,18 +272,27 @@ __device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float x
 }
 
 // O~^T += V^^T P^^T for 64-key chunk c, plus (PNQ) the row sum of the same P^ as a ones MFMA.
+// O~^T += V^^T P^^T for the 64-key chunk c (its V^ fragments read here, so only one
+// chunk's occupy registers), plus with PNQ the row sum of the same P^: r = its total.
 template <int D, bool PNQ>
-__device__ __forceinline__ void pv_mfma(v16f (&acc)[D / 32], v16f& rs, const v8i (&vf)[D / 32][2], int vsw,
-                                        const v8i& ones, const uint32_t (&pc)[4], int psc, int c) {
+__device__ __forceinline__ void pv_chunk(v16f (&acc)[D / 32], const uint8_t* __restrict__ st, int lane, int vsw,
+                                         int c, const v8i& ones, const uint32_t (&pc)[4], int psc, float& r) {
+  using G = Geo<D>;
   constexpr int NCT = D / 32;
-  const v8i pf = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
-  if constexpr (PNQ) rs = mma<0>(ones, pf, rs, 127, psc);
+  v8i vf[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    if (ct == 0) acc[ct] = mma<0>(vf[ct][c], pf, acc[ct], vsw, psc);
-    if (ct == 1) acc[ct] = mma<1>(vf[ct][c], pf, acc[ct], vsw, psc);
-    if (ct == 2) acc[ct] = mma<2>(vf[ct][c], pf, acc[ct], vsw, psc);
-    if (ct == 3) acc[ct] = mma<3>(vf[ct][c], pf, acc[ct], vsw, psc);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(st + G::OFF_VC + 1024 * (2 * ct + c) + 16 * lane);
+    vf[ct] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  }
+  const v8i pf = v8i{(int)pc[0], (int)pc[1], (int)pc[2], (int)pc[3], 0, 0, 0, 0};
+  if constexpr (PNQ) r = mma<0>(ones, pf, v16f{}, 127, psc)[0];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (ct == 0) acc[ct] = mma<0>(vf[ct], pf, acc[ct], vsw, psc);
+    if (ct == 1) acc[ct] = mma<1>(vf[ct], pf, acc[ct], vsw, psc);
+    if (ct == 2) acc[ct] = mma<2>(vf[ct], pf, acc[ct], vsw, psc);
+    if (ct == 3) acc[ct] = mma<3>(vf[ct], pf, acc[ct], vsw, psc);
   }
 }
 
@@ -301,15 +310,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   const int i = lane & 31;
   const int h = lane >> 5;
 
-  // K^ fragments and scales: MFMA (t, s) uses keys kappa(t, .), d-block 2s + h
-  v8i kf[4][S];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(st + 1024 * (S * t + s) + 16 * lane);
-      kf[t][s] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-    }
+  // K^ scales: MFMA (t, s) uses keys kappa(t, .), d-block 2s + h
   int ksw[S];
   if constexpr (PRE) {
     const u32x2 d = *reinterpret_cast<const u32x2*>(st + G::OFF_KS + 8 * lane);
@@ -320,20 +321,36 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     ksw[0] = (int)gather4(d, sel0);
     if constexpr (S == 2) ksw[1] = (int)gather4(d, sel1);
   }
-
   const v16f z = {};
   v16f x[4];
-  x[0] = mma<0>(kf[0][0], qf[0], z, ksw[0], qsc[0]);
-  x[1] = mma<1>(kf[1][0], qf[0], z, ksw[0], qsc[0]);
-  if constexpr (S == 2) {
-    x[0] = mma<0>(kf[0][1], qf[1], x[0], ksw[1], qsc[1]);
-    x[1] = mma<1>(kf[1][1], qf[1], x[1], ksw[1], qsc[1]);
-  }
-  x[2] = mma<2>(kf[2][0], qf[0], z, ksw[0], qsc[0]);
-  x[3] = mma<3>(kf[3][0], qf[0], z, ksw[0], qsc[0]);
-  if constexpr (S == 2) {
-    x[2] = mma<2>(kf[2][1], qf[1], x[2], ksw[1], qsc[1]);
-    x[3] = mma<3>(kf[3][1], qf[1], x[3], ksw[1], qsc[1]);
+  // K^ fragments read in two halves (keys of chunk 0, then chunk 1), each just before
+  // its MFMAs, so that only half of them occupy registers at a time
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    v8i kf[2][S];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(st + 1024 * (S * (2 * c + tt) + s) + 16 * lane);
+        kf[tt][s] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      }
+    if (c == 0) {
+      x[0] = mma<0>(kf[0][0], qf[0], z, ksw[0], qsc[0]);
+      x[1] = mma<1>(kf[1][0], qf[0], z, ksw[0], qsc[0]);
+      if constexpr (S == 2) {
+        x[0] = mma<0>(kf[0][1], qf[1], x[0], ksw[1], qsc[1]);
+        x[1] = mma<1>(kf[1][1], qf[1], x[1], ksw[1], qsc[1]);
+      }
+    } else {
+      x[2] = mma<2>(kf[0][0], qf[0], z, ksw[0], qsc[0]);
+      x[3] = mma<3>(kf[1][0], qf[0], z, ksw[0], qsc[0]);
+      if constexpr (S == 2) {
+        x[2] = mma<2>(kf[0][1], qf[1], x[2], ksw[1], qsc[1]);
+        x[3] = mma<3>(kf[1][1], qf[1], x[3], ksw[1], qsc[1]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   if constexpr (TAIL) {
@@ -357,15 +374,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     for (int v = 0; v < 16; ++v) x[t][v] = __builtin_fmaf(x[t][v], cl, -mc);
   const float xm0 = (bm0 - mnew) * cl, xm1 = (bm1 - mnew) * cl;
 
-  // V^ fragments (A operand of O^T): channels 32 ct + i, keys 64 c + 32 h .. +31
-  v8i vf[NCT][2];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(st + G::OFF_VC + 1024 * (2 * ct + c) + 16 * lane);
-      vf[ct][c] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-    }
+  // V^ scales (the fragments are read per chunk in pv_chunk)
   int vsw[2];
   if constexpr (PRE) {
     const u32x2 d = *reinterpret_cast<const u32x2*>(st + G::OFF_VS + 8 * lane);
@@ -397,13 +406,13 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
     for (int ct = 0; ct < NCT; ++ct) acc[ct] *= alpha;
   }
   __builtin_amdgcn_sched_barrier(0);
-  v16f rs = z;
-  pv_mfma<D, PNQ>(acc, rs, vf, vsw[0], ones, pc0, psc0, 0);
+  float r0 = 0.0f, r1 = 0.0f;
+  pv_chunk<D, PNQ>(acc, st, lane, vsw[0], 0, ones, pc0, psc0, r0);
   soft_exp<PNQ>(x[2], x[3], xm1, prule, pc1, psc1, ls);
   interleave_mfma<NCT + (PNQ ? 1 : 0), 6>();
   __builtin_amdgcn_sched_barrier(0);
-  pv_mfma<D, PNQ>(acc, rs, vf, vsw[1], ones, pc1, psc1, 1);
-  if constexpr (PNQ) l = __builtin_fmaf(l, alpha, rs[0]);
+  pv_chunk<D, PNQ>(acc, st, lane, vsw[1], 1, ones, pc1, psc1, r1);
+  if constexpr (PNQ) l = __builtin_fmaf(l, alpha, r0 + r1);
   else l = __builtin_fmaf(l, alpha, xsum2(ls));
 
   if constexpr (DUMP) {
@@ -510,7 +519,7 @@ __device__ __forceinline__ void quantise_q_blocks(const AttnArgs& a, int64_t row
 
 // One workgroup = NW waves of 32 queries.
 template <int D, bool PRE, bool PNQ, bool DUMP>
-__global__ __launch_bounds__(NT, 2) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
+__global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   using G = Geo<D>;
   constexpr int S = G::S;
   constexpr int NCT = G::NCT;
