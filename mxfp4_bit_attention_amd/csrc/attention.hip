@@ -223,12 +223,11 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf
 // Max of the 32 values of one block (a = keys 0..15, b = keys 16..31) with a max3 tree.
 __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
   auto x = [&](int k) { return k < 16 ? a[k] : b[k - 16]; };
-  float u[11];
+  float u[10];  // 16 max operations in three levels: 10, 4 and 2
 #pragma unroll
   for (int i = 0; i < 10; ++i) u[i] = fmax3(x(3 * i), x(3 * i + 1), x(3 * i + 2));
-  u[10] = fmaxf(x(30), x(31));
   const float w0 = fmax3(u[0], u[1], u[2]), w1 = fmax3(u[3], u[4], u[5]);
-  const float w2 = fmax3(u[6], u[7], u[8]), w3 = fmaxf(u[9], u[10]);
+  const float w2 = fmax3(u[6], u[7], u[8]), w3 = fmax3(u[9], x(30), x(31));
   return fmaxf(fmax3(w0, w1, w2), w3);
 }
 
@@ -372,6 +371,9 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[t][v] = __builtin_fmaf(x[t][v], cl, -mc);
+  // the block maxes' arguments as a difference first: exactly 0 in the block that holds
+  // the row max, whose P~ block max is then exactly 1 as the method defines it (an fma
+  // here can leave a rounding residue and move the floor rule's exponent)
   const float xm0 = (bm0 - mnew) * cl, xm1 = (bm1 - mnew) * cl;
 
   // V^ scales (the fragments are read per chunk in pv_chunk)
