@@ -196,6 +196,12 @@ def test_full_size_hunyuan720p_sampled_rows():
     _full_size_case(synth.HUNYUAN_720P)
 
 
+def test_full_size_d64_sampled_rows():
+    """The Wan2.2-720p token count at head dim 64 (the d = 64 kernel at full length)."""
+    w = dataclasses.replace(synth.WAN_720P, d=64, softmax_scale=0.125, name="wan2.2-720p-h40-n75600-d64")
+    _full_size_case(w)
+
+
 def test_repeatable_bitwise():
     torch, mx = require_gpu()
     g = torch.Generator(device="cuda").manual_seed(1)
