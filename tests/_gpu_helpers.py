@@ -40,17 +40,23 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-def p_code_mismatch(gpu_pc_packed: np.ndarray, gpu_ps: np.ndarray, ora_pc: np.ndarray, ora_ps: np.ndarray):
-    """Fraction of P^ codes that differ, a changed block exponent counting as all 32 codes."""
+def p_code_mismatch(gpu_pc_packed: np.ndarray, gpu_ps: np.ndarray, ora_pc: np.ndarray, ora_ps: np.ndarray,
+                    nkv: int):
+    """Fraction of the P^ codes of the first nkv keys that differ, a changed block
+    exponent counting as all of that block's codes among those keys.  Keys past nkv
+    (padding, code 0 on both sides) are left out of numerator and denominator alike."""
     g = mxfp4.unpack_nibbles(gpu_pc_packed)
     n = g.shape[-1]
-    assert ora_pc.shape[-1] == n
-    gb = g.reshape(g.shape[:-1] + (n // 32, 32))
-    ob = ora_pc.reshape(ora_pc.shape[:-1] + (n // 32, 32))
-    scale_diff = gpu_ps != ora_ps
-    code_diff = (gb != ob).sum(axis=-1)
-    bad = np.where(scale_diff, 32, code_diff).sum()
-    return float(bad) / g.size
+    assert ora_pc.shape[-1] == n and 0 < nkv <= n
+    nb = -(-nkv // 32)
+    gb = g[..., : nb * 32].reshape(g.shape[:-1] + (nb, 32))
+    ob = ora_pc[..., : nb * 32].reshape(ora_pc.shape[:-1] + (nb, 32))
+    real = np.minimum(32, nkv - 32 * np.arange(nb))            # real keys in each block
+    keep = np.arange(32)[None, :] < real[:, None]               # [nb, 32]
+    scale_diff = gpu_ps[..., :nb] != ora_ps[..., :nb]
+    code_diff = ((gb != ob) & keep).sum(axis=-1)
+    bad = np.where(scale_diff, real, code_diff).sum()
+    return float(bad) / (np.prod(g.shape[:-1]) * nkv)
 
 
 RULES = {"uos": ("uos", mxfp4.UOS), "ocp": ("ocp", mxfp4.OCP), "tfs": (("ceil", 6.0), mxfp4.TFS),

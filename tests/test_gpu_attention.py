@@ -76,7 +76,7 @@ def test_quantized_entry_p_codes(rule, Nq, Nkv, d):
     Oo, opc, ops = ora.flash_attention_mx(*q, Nkv, scale, True, RULES[rule][1], Bc, return_p=True)
     err = rel_l2(O.cpu().numpy()[0, 0], Oo)
     assert err < REL_L2, f"rel-L2 {err:.2e}"
-    mm = p_code_mismatch(u8(pc)[0, 0], u8(ps)[0, 0], opc, ops)
+    mm = p_code_mismatch(u8(pc)[0, 0], u8(ps)[0, 0], opc, ops, Nkv)
     assert mm < P_MISMATCH, f"P^ code mismatch {mm:.2e}"
 
 

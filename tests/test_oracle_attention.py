@@ -7,7 +7,18 @@
 * Direct placement (Figure 4(C)) and post-normalisation (Figure 4(A), Figure
   7(A)) visibly break the sum-to-one property.
 * Convexity: with PNQ, O is a convex combination of the dequantised V rows.
-* Single tile: at Bc >= N_kv the running max is the global max.
+* Single tile: at Bc >= N_kv the running max is the global max, and the flash
+  oracle equals a materialised global-max P^ element by element.
+* The multi-tile rescale alpha = exp(m - m') (FA-2 recurrence; Pith review,
+  Axiom ledger axiom 4 and Figure 4(B) caption), pinned two ways that do not
+  reuse the recurrence:
+    - power-of-two equivariance: with softmax_scale = ln 2 and integer logits,
+      every running-max step is a whole number of octaves, the block quantiser
+      commutes with the factor 2^k (its scale rule is power-of-two equivariant),
+      so every tile width must give the single-tile result to rounding;
+    - the unrolled closed form O = sum_j w_j P^_j V^_j / sum_j w_j rowsum(P^_j),
+      w_j = exp(m_j - m_last), P^_j quantised at the prefix max m_j.
+  Setting alpha to 1, or to exp(m' - m), fails both.
 * Structural invariants: row independence, scale equivariance.
 """
 import numpy as np
@@ -108,7 +119,7 @@ def test_on_grid_operands_quantise_exactly():
     assert (Kd == Kv).all() and (Vd == Vv).all()
     Oe = attention.exact_attention(Qd, Kd, Vd, 0.125)
     rel = np.linalg.norm(O - Oe) / np.linalg.norm(Oe)
-    assert 0 < rel < 0.5
+    assert 0.05 < rel < 0.15                                   # measured 0.0996 (a guard, not a pin)
 
 
 def test_rows_are_independent_and_selectable():
@@ -158,5 +169,118 @@ def test_pipeline_hadamard_changes_codes_not_logits():
     Oe = attention.exact_attention(Q, K, V, w.softmax_scale)
     e_h = np.linalg.norm(O_h - Oe) / np.linalg.norm(Oe)
     e_n = np.linalg.norm(O_n - Oe) / np.linalg.norm(Oe)
-    assert 0 < e_h < 1.5 and 0 < e_n < 1.5 and e_h != e_n
+    # measured 0.898 and 0.969: at this tiny shape MXFP4 noise in Q^ and K^ dominates O's error against
+    # exact attention (a guard on the pipeline's wiring, not a pin: the pages print no tensor error)
+    assert 0.8 < e_h < 1.0 and 0.85 < e_n < 1.1 and e_h != e_n
     assert np.abs(hadamard.fwht_fp32(Q) @ hadamard.fwht_fp32(K).T - Q @ K.T).max() < 1e-2
+
+
+# ---- the multi-tile rescale and the single-tile identity --------------------------
+
+def _materialised_global_max(Qd, Kd, V, scale, pnq, rule):
+    """One tile holding every key: m = the row's global max, P~ = fl32(exp(S - m)),
+    P^ by 32-key blocks, O = P^ V / (row sum of P^, or of P~ with direct placement)."""
+    S = scale * (Qd @ Kd.T)
+    P = np.exp(S - S.max(axis=1, keepdims=True)).astype(np.float32)
+    n = S.shape[1]
+    Pp = np.zeros((S.shape[0], -(-n // 32) * 32), np.float32)
+    Pp[:, :n] = P
+    pc, ps = mxfp4.quantize_blocks_lastaxis(Pp, rule)
+    Ph = mxfp4.dequantize_blocks_lastaxis(pc, ps)[:, :n]
+    denom = Ph.sum(axis=1) if pnq else P.astype(np.float64).sum(axis=1)
+    return (Ph @ V) / denom[:, None], pc, ps
+
+
+@pytest.mark.parametrize("rule", list(RULES))
+@pytest.mark.parametrize("pnq", [True, False])
+@pytest.mark.parametrize("Bc", [256, 512])
+def test_single_tile_equals_materialised_global_max(rule, pnq, Bc):
+    Q, K, V, w = _tiny_inputs()
+    q = _quantized(Q, K, V, RULES[rule], True, v_pad=256)
+    O, pc, ps = attention.flash_attention_mx(*q, w.N, w.softmax_scale, pnq, RULES[rule], Bc, return_p=True)
+    Qd = mxfp4.dequantize_blocks_lastaxis(q[0], q[1])
+    Kd = mxfp4.dequantize_blocks_lastaxis(q[2], q[3])
+    Vd = mxfp4.dequantize_blocks_lastaxis(q[4], q[5]).T[: w.N]
+    Om, mpc, mps = _materialised_global_max(Qd, Kd, Vd, w.softmax_scale, pnq, RULES[rule])
+    assert (pc[:, : w.N] == mpc[:, : w.N]).all() and (ps[:, : w.N // 32] == mps).all()
+    assert np.abs(O - Om).max() <= 1e-13 * np.abs(Om).max()
+
+
+def _octave_case(seed, nq=6, nkv=256, d=64):
+    """Integer-valued MXFP4 operands whose logits (in units of softmax_scale) are
+    integers, arranged so that each row's running max grows over the first tiles.
+    Q rows are unit or two-unit vectors on channels 0..3; keys of 32-key group t use
+    values of magnitude <= 1, 2, 3, 4, 6, 6, ... on those channels."""
+    rng = np.random.default_rng(seed)
+    ints = np.array([0, 1, 2, 3, 4, 6, -1, -2, -3, -4, -6], float)
+    Q = np.zeros((nq, d))
+    for r in range(nq):
+        Q[r, r % 4] = 1.0
+        if r >= 4:
+            Q[r, (r + 1) % 4] = -1.0
+    K = np.zeros((nkv, d))
+    for k in range(nkv):
+        hi = [1, 2, 3, 4, 6][min(k // 32, 4)]
+        K[k, :4] = rng.choice(ints[np.abs(ints) <= hi], 4)
+    V = rng.standard_normal((nkv, d))
+    return Q, K, V
+
+
+@pytest.mark.parametrize("rule", list(RULES))
+@pytest.mark.parametrize("pnq", [True, False])
+def test_octave_running_max_steps_make_every_tile_width_agree(rule, pnq):
+    """softmax_scale = ln 2 and integer Q^K^T: every P~ = exp(S - m') is a power of two
+    (rounded to fp32 from float64 it is exactly one), every step of the running max is
+    a whole number of octaves, and a block-quantised tile scaled by 2^k is the tile
+    quantised then scaled by 2^k (the shared exponent moves by k under every rule).
+    So the FA-2 recurrence must give the single-tile output for every tile width, to
+    float64 rounding; a wrong rescale factor weights the early tiles by 2^k."""
+    Q, K, V = _octave_case(11)
+    r = RULES[rule]
+    Qc, Qs = mxfp4.quantize_blocks_lastaxis(Q, r)
+    Kc, Ks = mxfp4.quantize_blocks_lastaxis(K, r)
+    assert (mxfp4.dequantize_blocks_lastaxis(Qc, Qs) == Q).all()
+    assert (mxfp4.dequantize_blocks_lastaxis(Kc, Ks) == K).all()
+    Vc, Vs = mxfp4.quantize_rows_transposed(V, r, 256)
+    scale = float(np.log(2.0))
+    n = Q @ K.T
+    steps = [(np.diff([n[i, : 32 * (t + 1)].max() for t in range(8)]) > 0).sum() for i in range(len(Q))]
+    assert min(steps) >= 3                                    # the running max moves on >= 3 tiles per row
+    O1 = attention.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, 256, scale, pnq, r, 256)
+    for Bc in (32, 64, 96, 128):
+        O = attention.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, 256, scale, pnq, r, Bc)
+        assert np.abs(O - O1).max() < 1e-13, Bc
+
+
+@pytest.mark.parametrize("rule", ["uos", "ocp"])
+@pytest.mark.parametrize("pnq", [True, False])
+def test_unrolled_closed_form_of_the_recurrence(rule, pnq):
+    """O after the last tile equals sum_j w_j P^_j V^_j / sum_j w_j l_j with
+    w_j = exp(m_j - m_last), P^_j = Q(fl32(exp(S_j - m_j))) quantised at the prefix max
+    m_j, and l_j its row sum (or the row sum of P~_j with direct placement): the FA-2
+    recurrence written out without recursion, on the tiny workload's logits."""
+    Q, K, V, w = _tiny_inputs(1)
+    r = RULES[rule]
+    q = _quantized(Q, K, V, r, True, v_pad=256)
+    Bc = 32
+    O = attention.flash_attention_mx(*q, w.N, w.softmax_scale, pnq, r, Bc)
+    Qd = mxfp4.dequantize_blocks_lastaxis(q[0], q[1])
+    Kd = mxfp4.dequantize_blocks_lastaxis(q[2], q[3])
+    Vd = mxfp4.dequantize_blocks_lastaxis(q[4], q[5]).T[: w.N]
+    S = w.softmax_scale * (Qd @ Kd.T)
+    tiles = [slice(j, j + Bc) for j in range(0, w.N, Bc)]
+    prefix = np.stack([S[:, : t.stop].max(axis=1) for t in tiles], axis=1)     # m_j
+    num = np.zeros_like(O)
+    den = np.zeros(len(O))
+    moved = 0
+    for j, t in enumerate(tiles):
+        P = np.exp(S[:, t] - prefix[:, j:j + 1]).astype(np.float32)
+        pc, ps = mxfp4.quantize_blocks_lastaxis(P, r)
+        Ph = mxfp4.dequantize_blocks_lastaxis(pc, ps)
+        wj = np.exp(prefix[:, j] - prefix[:, -1])
+        num += wj[:, None] * (Ph @ Vd[t])
+        den += wj * (Ph.sum(axis=1) if pnq else P.astype(np.float64).sum(axis=1))
+        moved += int((wj < 1).sum())
+    assert moved > len(O)                                     # the prefix max moves for many rows
+    Oc = num / den[:, None]
+    assert np.abs(O - Oc).max() <= 1e-12 * np.abs(Oc).max()

@@ -94,6 +94,63 @@ def test_rowsum_direct_placement_drifts_down():
     assert dec["total"] < 0 and dec["zeroed"] < 0
 
 
+def _key_row(logit):
+    """A key row of 32 E2M1 values times 2^-4 whose dot product with an all-ones query
+    is `logit` (a multiple of 1/32, |logit| <= 12)."""
+    t, vals = logit * 16.0, []
+    for _ in range(32):
+        a = max(x for x in mxfp4.E2M1_GRID if x <= min(abs(t), 6.0))
+        vals.append(np.copysign(a, t))
+        t -= vals[-1]
+    assert t == 0.0
+    return np.array(vals) * 2.0 ** -4
+
+
+# One query row, one kv tile of 64 keys (two 32-key blocks), logits chosen by hand so that
+# each element's scaled value P~ / 2^e sits well inside one rounding class.  Block 0 holds
+# the row max (P~ = 1, UOS exponent -2: scaled values are 4 P~); block 1's largest P~ is
+# exp(-0.125) = 0.882, whose UOS exponent is -3 (0.882 * 8 = 7.06 <= 7.25).  Each entry:
+# (logit, block, P^ value from the E2M1 table, class).
+CLASS_TILE = [
+    (10.0, 0, 1.0, None),                        # scaled 4      -> 4, exact
+    (7.0, 0, 0.0, "zeroed"),                     # scaled 0.199  -> 0
+    (8.71875, 0, 1.0 * 2 ** -2, "rounded_down"),  # scaled 1.110  -> 1
+    (9.59375, 0, 3.0 * 2 ** -2, "rounded_up"),    # scaled 2.664  -> 3
+    (8.09375, 0, 0.5 * 2 ** -2, "rounded_down"),  # scaled 0.594  -> 0.5
+    (7.5625, 0, 0.5 * 2 ** -2, "rounded_up"),     # scaled 0.350  -> 0.5
+    (9.875, 1, 6.0 * 2 ** -3, "saturated"),       # scaled 7.06   -> 8 unbounded, 6 in E2M1
+    (9.8125, 1, 6.0 * 2 ** -3, "rounded_down"),   # scaled 6.63   -> 6 (below the tie at 7)
+    (9.625, 1, 6.0 * 2 ** -3, "rounded_up"),      # scaled 5.50   -> 6
+    (9.40625, 1, 4.0 * 2 ** -3, "rounded_down"),  # scaled 4.42   -> 4
+    (5.625, 1, 0.0, "zeroed"),                    # scaled 0.101  -> 0
+]
+
+
+def test_rowsum_classes_on_a_hand_built_tile():
+    """Each class of rowsum_decomposition against sums written out from the table above:
+    the class of an element is fixed by its scaled value (zeroed: code 0 for P~ > 0;
+    saturated: scaled >= 7, where round-to-nearest heads for 8 and the format clips to
+    6; otherwise the sign of P^ - P~), so a shifted boundary or a swapped class fails."""
+    n0 = sum(1 for e in CLASS_TILE if e[1] == 0)
+    logits = [e[0] for e in CLASS_TILE if e[1] == 0] + [10.0] * (32 - n0) + [e[0] for e in CLASS_TILE if e[1] == 1]
+    nkv = len(logits)                                     # keys 37..63 of the tile are padding
+    K = np.stack([_key_row(x) for x in logits])
+    Q = np.ones((1, 32))
+    Qc, Qs = mxfp4.quantize_blocks_lastaxis(Q, mxfp4.UOS)
+    Kc, Ks = mxfp4.quantize_blocks_lastaxis(K, mxfp4.UOS)
+    assert (mxfp4.dequantize_blocks_lastaxis(Kc, Ks) @ Q[0] == np.array(logits)).all()
+    dec = od.rowsum_decomposition(Qc, Qs, Kc, Ks, nkv, 1.0, mxfp4.UOS, 64)
+    P = {x: float(np.float32(np.exp(x - 10.0))) for x in logits}
+    lt = sum(P[x] for x in logits)
+    want = {c: 0.0 for c in ("zeroed", "saturated", "rounded_down", "rounded_up")}
+    for logit, _, ph, cls in CLASS_TILE:
+        if cls:
+            want[cls] += ph - P[logit]
+    for c, v in want.items():
+        assert dec[c] == pytest.approx(v / lt, rel=1e-12, abs=1e-15), c
+    assert dec["total"] == pytest.approx(sum(want.values()) / lt, rel=1e-12)
+
+
 # ---- global-scaling arm (post-normalisation P, one factor g before quantisation)
 
 def test_global_scaling_one_hot_rows_closed_form():
