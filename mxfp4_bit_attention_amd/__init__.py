@@ -141,10 +141,54 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _need_cuda(*ts):
-    for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("tensors must be contiguous and on the GPU")
+def _expect(t, name: str, shape, dtypes):
+    """Shape and dtype of one caller tensor (checked before anything touches the GPU)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        names = ", ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be {names}, got {str(t.dtype).replace('torch.', '')}")
+
+
+def _on_device(device, **named):
+    """Every named tensor contiguous and on `device` (a CUDA device)."""
+    if device.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    for name, t in named.items():
+        if t is None:
+            continue
+        if t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _float_dtypes():
+    torch = _torch()
+    return (torch.float32, torch.bfloat16)
+
+
+def _u8():
+    return (_torch().uint8,)
+
+
+def _as3(x):
+    if x.dim() == 2:
+        return x.unsqueeze(0), True
+    if x.dim() == 3:
+        return x, False
+    raise ValueError("x must be 2-D or 3-D")
+
+
+def _quant_shapes(b, r, c, axis):
+    if axis == "last":
+        return MXATTN_AXIS_LAST, (b, r, c // 2), (b, r, c // 32)
+    if axis == "rows":
+        P = mxattn_padded_tokens(r)
+        return MXATTN_AXIS_ROWS, (b, c, P // 2), (b, c, P // 32)
+    raise ValueError("axis must be 'last' or 'rows'")
 
 
 def mxattn_quantize(x, rule="uos", axis: str = "last", hadamard: bool = False, codes=None, scales=None):
@@ -152,28 +196,25 @@ def mxattn_quantize(x, rule="uos", axis: str = "last", hadamard: bool = False, c
 
     axis="last": codes [batch, rows, cols/2], scales [batch, rows, cols/32].
     axis="rows": codes [batch, cols, P/2], scales [batch, cols, P/32], P = mxattn_padded_tokens(rows).
+    codes / scales, when given, must have exactly those shapes (uint8, contiguous, on x's device).
     """
     torch = _torch()
-    _need_cuda(x)
-    squeeze = x.dim() == 2
-    x3 = x.unsqueeze(0) if squeeze else x
-    if x3.dim() != 3:
-        raise ValueError("x must be 2-D or 3-D")
+    x3, squeeze = _as3(x)
+    _expect(x3, "x", x3.shape, _float_dtypes())
     b, r, c = x3.shape
-    if axis == "last":
-        ax = MXATTN_AXIS_LAST
-        cshape, sshape = (b, r, c // 2), (b, r, c // 32)
-    elif axis == "rows":
-        ax = MXATTN_AXIS_ROWS
-        P = mxattn_padded_tokens(r)
-        cshape, sshape = (b, c, P // 2), (b, c, P // 32)
-    else:
-        raise ValueError("axis must be 'last' or 'rows'")
+    ax, cshape, sshape = _quant_shapes(b, r, c, axis)
+    # a 2-D x takes 2-D (or leading-1 3-D) codes and scales
+    if codes is not None:
+        _expect(codes, "codes", cshape[1:] if squeeze and codes.dim() == 2 else cshape, _u8())
+    if scales is not None:
+        _expect(scales, "scales", sshape[1:] if squeeze and scales.dim() == 2 else sshape, _u8())
+    _on_device(x.device, x=x3, codes=codes, scales=scales)
+    codes = codes.view(cshape) if codes is not None else None
+    scales = scales.view(sshape) if scales is not None else None
     if codes is None:
         codes = torch.empty(cshape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(sshape, dtype=torch.uint8, device=x.device)
-    _need_cuda(codes, scales)
     kind, q = rule_args(rule)
     _check(LIB.mxattn_quantize(_ptr(x3), _dtype_code(x3), b, r, c, ax, kind, q, int(bool(hadamard)),
                                _ptr(codes), _ptr(scales), _stream(x.device)))
@@ -190,17 +231,15 @@ def mxattn_quant_error(x, rule="uos", axis: str = "last", hadamard: bool = False
     when hadamard is set).
     """
     torch = _torch()
-    _need_cuda(x)
-    x3 = x.unsqueeze(0) if x.dim() == 2 else x
-    if x3.dim() != 3:
-        raise ValueError("x must be 2-D or 3-D")
+    x3, _ = _as3(x)
+    _expect(x3, "x", x3.shape, _float_dtypes())
     b, r, c = x3.shape
-    ax = {"last": MXATTN_AXIS_LAST, "rows": MXATTN_AXIS_ROWS}.get(axis)
-    if ax is None:
-        raise ValueError("axis must be 'last' or 'rows'")
+    ax = _quant_shapes(b, r, c, axis)[0]
+    if sums is not None:
+        _expect(sums, "sums", (3,), (torch.float64,))
+    _on_device(x.device, x=x3, sums=sums)
     if sums is None:
         sums = torch.empty(3, dtype=torch.float64, device=x.device)
-    _need_cuda(sums)
     kind, q = rule_args(rule)
     _check(LIB.mxattn_quant_error(_ptr(x3), _dtype_code(x3), b, r, c, ax, kind, q, int(bool(hadamard)),
                                   _ptr(sums), _stream(x.device)))
@@ -209,19 +248,29 @@ def mxattn_quant_error(x, rule="uos", axis: str = "last", hadamard: bool = False
 
 def mxattn_forward(q, k, v, softmax_scale: float, hadamard: bool = True, pnq: bool = True, rule="uos",
                    out=None, workspace=None):
-    """O = MXFP4 attention of q [B,H,Nq,d], k, v [B,H,Nkv,d] (fp32 or bf16), same dtype out."""
+    """O = MXFP4 attention of q [B,H,Nq,d], k, v [B,H,Nkv,d] (fp32 or bf16), same dtype out.
+
+    out, when given: [B,H,Nq,d] in q's dtype.  workspace, when given: uint8, at least
+    mxattn_forward_workspace_bytes(B, H, Nq, Nkv, d) elements.  All on q's device, contiguous."""
     torch = _torch()
-    _need_cuda(q, k, v)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
     B, H, Nq, d = q.shape
     Nkv = k.shape[2]
-    if k.shape != (B, H, Nkv, d) or v.shape != (B, H, Nkv, d) or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("k and v must be [B, H, Nkv, d] with q's dtype")
+    _expect(q, "q", q.shape, _float_dtypes())
+    _expect(k, "k", (B, H, Nkv, d), (q.dtype,))
+    _expect(v, "v", (B, H, Nkv, d), (q.dtype,))
+    if out is not None:
+        _expect(out, "out", (B, H, Nq, d), (q.dtype,))
+    wsb = mxattn_forward_workspace_bytes(B, H, Nq, Nkv, d)
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-D uint8 tensor")
+        if workspace.numel() < wsb:
+            raise ValueError(f"workspace has {workspace.numel()} bytes, needs {wsb}")
+    _on_device(q.device, q=q, k=k, v=v, out=out, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
-    _need_cuda(out)
-    wsb = mxattn_forward_workspace_bytes(B, H, Nq, Nkv, d)
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=q.device)
     kind, qm = rule_args(rule)
@@ -231,22 +280,55 @@ def mxattn_forward(q, k, v, softmax_scale: float, hadamard: bool = True, pnq: bo
     return out
 
 
+def _quantized_operands(qc, qs, kc, kscales, vtc, vscales, Nkv: int, arranged: bool):
+    """Shapes of the MXFP4 operands of the attention entries: (B, H, Nq, d)."""
+    if qc is None or qc.dim() != 4:
+        raise ValueError("qc must be [B, H, Nq, d/2]")
+    B, H, Nq, dh = qc.shape
+    d = 2 * dh
+    Nkv = int(Nkv)
+    if Nkv < 1:
+        raise ValueError("Nkv must be >= 1")
+    P = mxattn_padded_tokens(Nkv)
+    u8 = _u8()
+    _expect(qc, "qc", (B, H, Nq, d // 2), u8)
+    _expect(qs, "qs", (B, H, Nq, d // 32), u8)
+    _expect(kc, "kc", (B, H, Nkv, d // 2), u8)
+    _expect(vtc, "vtc", (B, H, d, P // 2), u8)
+    if arranged:
+        _expect(kscales, "ksa", (B, H, P * 4), u8)
+        _expect(vscales, "vtsa", (B, H, P * 4), u8)
+    else:
+        _expect(kscales, "ks", (B, H, Nkv, d // 32), u8)
+        _expect(vscales, "vts", (B, H, d, P // 32), u8)
+    return B, H, Nq, d
+
+
+def _attn_out(out, out_dtype, shape, device):
+    torch = _torch()
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    if out_dtype not in _float_dtypes():
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is not None:
+        _expect(out, "out", shape, (out_dtype,))
+    return out, out_dtype
+
+
 def mxattn_forward_quantized(qc, qs, kc, ks, vtc, vts, Nkv: int, softmax_scale: float, pnq: bool = True,
                              p_rule="uos", out_dtype=None, out=None, dump_p: bool = False):
     """Attention on MXFP4 operands in the layouts of mxattn_quantize.
 
-    qc [B,H,Nq,d/2], qs [B,H,Nq,d/32], kc [B,H,Nkv,d/2], ks, vtc [B,H,d,P/2], vts [B,H,d,P/32].
-    Returns O [B,H,Nq,d] (and, with dump_p, the P^ codes [B,H,Nq,P/2] and scales [B,H,Nq,P/32]).
+    qc [B,H,Nq,d/2], qs [B,H,Nq,d/32], kc [B,H,Nkv,d/2], ks [B,H,Nkv,d/32], vtc [B,H,d,P/2],
+    vts [B,H,d,P/32] (uint8, P = mxattn_padded_tokens(Nkv)).  Returns O [B,H,Nq,d] (and, with
+    dump_p, the P^ codes [B,H,Nq,P/2] and scales [B,H,Nq,P/32]).
     """
     torch = _torch()
-    _need_cuda(qc, qs, kc, ks, vtc, vts)
-    B, H, Nq, dh = qc.shape
-    d = dh * 2
-    if out_dtype is None:
-        out_dtype = torch.float32
+    B, H, Nq, d = _quantized_operands(qc, qs, kc, ks, vtc, vts, Nkv, arranged=False)
+    out, out_dtype = _attn_out(out, out_dtype, (B, H, Nq, d), qc.device)
+    _on_device(qc.device, qc=qc, qs=qs, kc=kc, ks=ks, vtc=vtc, vts=vts, out=out)
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=qc.device)
-    _need_cuda(out)
     P = mxattn_padded_tokens(Nkv)
     pc = ps = None
     if dump_p:
@@ -266,12 +348,17 @@ def mxattn_arrange_scales(ks, vts, Nkv: int):
     """ks [B,H,Nkv,d/32], vts [B,H,d,P/32] -> (ksa, vtsa), uint8 [B,H,P*4] each, in the
     per-kv-tile order of the attention kernel's MFMA scale operands."""
     torch = _torch()
-    _need_cuda(ks, vts)
-    B, H, nk, dg = ks.shape
+    if ks is None or ks.dim() != 4:
+        raise ValueError("ks must be [B, H, Nkv, d/32]")
+    B, H, _, dg = ks.shape
     d = dg * 32
+    Nkv = int(Nkv)
+    if Nkv < 1:
+        raise ValueError("Nkv must be >= 1")
     P = mxattn_padded_tokens(Nkv)
-    if nk != Nkv or tuple(vts.shape) != (B, H, d, P // 32):
-        raise ValueError("ks must be [B, H, Nkv, d/32] and vts [B, H, d, P/32]")
+    _expect(ks, "ks", (B, H, Nkv, d // 32), _u8())
+    _expect(vts, "vts", (B, H, d, P // 32), _u8())
+    _on_device(ks.device, ks=ks, vts=vts)
     ksa = torch.empty((B, H, P * 4), dtype=torch.uint8, device=ks.device)
     vtsa = torch.empty((B, H, P * 4), dtype=torch.uint8, device=ks.device)
     _check(LIB.mxattn_arrange_scales(_ptr(ks), _ptr(vts), B, H, Nkv, d, _ptr(ksa), _ptr(vtsa),
@@ -281,16 +368,14 @@ def mxattn_arrange_scales(ks, vts, Nkv: int):
 
 def mxattn_forward_arranged(qc, qs, kc, ksa, vtc, vtsa, Nkv: int, softmax_scale: float, pnq: bool = True,
                             p_rule="uos", out_dtype=None, out=None):
-    """mxattn_forward_quantized on scales from mxattn_arrange_scales (no P^ dump)."""
+    """mxattn_forward_quantized on scales from mxattn_arrange_scales (no P^ dump):
+    ksa and vtsa are uint8 [B,H,P*4]."""
     torch = _torch()
-    _need_cuda(qc, qs, kc, ksa, vtc, vtsa)
-    B, H, Nq, dh = qc.shape
-    d = dh * 2
-    if out_dtype is None:
-        out_dtype = torch.float32
+    B, H, Nq, d = _quantized_operands(qc, qs, kc, ksa, vtc, vtsa, Nkv, arranged=True)
+    out, out_dtype = _attn_out(out, out_dtype, (B, H, Nq, d), qc.device)
+    _on_device(qc.device, qc=qc, qs=qs, kc=kc, ksa=ksa, vtc=vtc, vtsa=vtsa, out=out)
     if out is None:
         out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=qc.device)
-    _need_cuda(out)
     kind, qm = rule_args(p_rule)
     _check(LIB.mxattn_forward_arranged(_ptr(qc), _ptr(qs), _ptr(kc), _ptr(ksa), _ptr(vtc), _ptr(vtsa),
                                        B, H, Nq, Nkv, d, float(softmax_scale), int(bool(pnq)), kind, qm,

@@ -23,8 +23,12 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxattn.so")
+# the microbenchmarks behind the benchmark's measured roofline denominators, kept out of
+# the attention library itself
+PROBES_LIB = os.path.join(HERE, "libmxattn_probes.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["quantize.hip", "attention.hip", "api.cpp"]
+PROBE_SOURCES = ["probes.hip"]
 # The attention kernel never sees a NaN it must propagate (inputs are finite
 # MXFP4 codes, masked keys use -inf), so its max reductions need no NaN
 # canonicalisation of every MFMA output.
@@ -49,10 +53,18 @@ def common_flags() -> list[str]:
     ]
 
 
+def _link(cc: str, objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    objs = []
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, src + ".o")
@@ -64,14 +76,10 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    _link(cc, objs[: len(SOURCES)], LIB)
+    _link(cc, objs[len(SOURCES):], PROBES_LIB)
     return LIB
 
 
