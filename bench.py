@@ -7,22 +7,33 @@ UOS quantisation of K along d, UOS quantisation of V along tokens, the re-orderi
 of their scale bytes into the attention kernel's per-tile operand order, and the
 fused MXFP4 flash attention with PNQ, which rotates and quantises Q itself as it
 loads its query rows.  Throughput is 4 B H N_q N_kv d per step time, in TFLOP/s.
+Each of the K timed steps is bracketed by its own HIP events on the launch stream
+(median, min and max reported beside the mean that gives `value`).
 
 Printed as one JSON line, with:
   roofline       the attention kernel (dominant) against the dense MXFP4 MFMA
-                 peak, timed alone (through mxattn_forward_arranged, the same
-                 kernel binary) with HIP events on its stream, plus HBM
-                 traffic from the committed rocprofv3 counter summary when it
-                 was taken on the current kernel source (else null);
+                 peak -- the metric's denominator -- timed alone (through
+                 mxattn_forward_arranged, the same kernel binary) with HIP events
+                 on its stream, plus HBM traffic from the committed rocprofv3
+                 counter summary when it was taken on the current kernel source
+                 (else null); `frac_measured` prices it against the fp4 MFMA rate
+                 measured on this board, and `alu_floor` against the issue-time
+                 floor of its softmax instructions (what binds it);
+  denominators   the microbenchmarks behind those figures (libmxattn_probes.so):
+                 fp4 MFMA rate and clock, per-instruction issue cycles, HBM
+                 read / copy bandwidth;
   quantize_pass  the standalone Hadamard + quantise pass on 40 x 75,600 x 128
-                 bf16 against HBM bandwidth (UOS, OCP and q = 6);
+                 bf16 (the seeded host law the parity test checks bit for bit)
+                 against HBM bandwidth (UOS, OCP and q = 6);
   rule_ablation  the full step under each shared-exponent rule (UOS, OCP, TFS,
                  OAS and CEIL 7.5; the same rule for Q, K, V and P~);
   other_shapes   the full step at d = 64, at B = 2 x H = 20, with 512 keys
                  (cross-attention-like), and on the Wan2.2-480p and
                  HunyuanVideo-720p workloads;
   cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
-                 on this host, extrapolated to the full workload.
+                 on this host, extrapolated to the full workload (and, under
+                 cpu_baseline_other, the same for Wan2.2-480p and for
+                 HunyuanVideo-720p's 256 text rows).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline] [--no-extras]
     python bench.py --traffic-probe     (one copy of known size + one attention
@@ -99,20 +110,61 @@ def time_launches(torch, fn, iters: int, stream) -> float:
     return e0.elapsed_time(e1) / iters
 
 
-def cpu_baseline(w) -> dict:
+def time_each(torch, fn, iters: int, stream) -> list:
+    """ms of each of `iters` back-to-back calls of fn(): one HIP event between calls on
+    `stream` (the events do not stall the stream), synchronised on both sides."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(iters):
+        fn()
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+
+
+def spread(ms: list) -> dict:
+    srt = sorted(ms)
+    n = len(srt)
+    med = srt[n // 2] if n % 2 else 0.5 * (srt[n // 2 - 1] + srt[n // 2])
+    return {"mean": round(sum(ms) / n, 3), "median": round(med, 3), "min": round(srt[0], 3),
+            "max": round(srt[-1], 3), "n": n}
+
+
+def alu_floor(den: dict, d: int) -> dict:
+    """Issue-time floor of the attention kernel's softmax: per score one FMA ((S - m')
+    scale log2 e), one exponential, half an fp4 conversion (two codes per instruction)
+    and half a max3 (two values per instruction of the block-max tree), at the cycles
+    per wave64 instruction per SIMD measured with three waves per SIMD.  A SIMD's wave
+    handles 64 scores per lane per 32-query x 128-key tile; the floor is the TFLOP/s
+    at which that issue time alone fills every SIMD at the probes' clock."""
+    v = den["valu_cycles_per_instruction_per_simd"]
+    c = {k: v[k]["cycles_3w"] for k in v}
+    per_tile = 64 * (c["v_exp_f32"] + c["v_fma_f32"]) + 32 * (c["v_cvt_scalef32_pk_fp4_f32"] + c["v_max3_f32"])
+    clock = 0.5 * (v["v_exp_f32"]["clock_MHz_3w"] + v["v_cvt_scalef32_pk_fp4_f32"]["clock_MHz_3w"]) * 1e6
+    simds = 4 * den["compute_units"]
+    flop_per_tile = 4.0 * 32 * 128 * d
+    return {"cycles_per_wave_tile": round(per_tile, 1), "clock_MHz": round(clock / 1e6, 1),
+            "peak_TFLOPs": round(flop_per_tile * simds * clock / per_tile / 1e12, 1)}
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing or failing: report the affinity count
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, rows: int = 1024, row_start: int = 0) -> dict:
     """The oracle on head 0: K and V quantisation of the full head, Q quantisation and
-    flash attention for 1024 query rows against all N_kv keys (about 10 s of CPU work);
+    flash attention for `rows` query rows (from `row_start`) against all N_kv keys;
     extrapolated to every row block and head."""
     import numpy as np
     from oracle import attention as ora
     from oracle import mxfp4
-    try:
-        from threadpoolctl import threadpool_info
-        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing or failing: report the affinity count
-        blas = len(os.sched_getaffinity(0))
-    rows = 1024
-    Q = synth.attn_head(w, synth.Q_ID, 0)[:rows]
+    blas = _blas_threads()
+    Q = synth.attn_head(w, synth.Q_ID, 0)[row_start:row_start + rows]
     K = synth.attn_head(w, synth.K_ID, 0)
     V = synth.attn_head(w, synth.V_ID, 0)
     P = -(-w.N // 128) * 128
@@ -137,10 +189,10 @@ def cpu_baseline(w) -> dict:
         "cores": int(blas),
         "kind": "oracle",
         "sample": (f"head 0 of {w.name}: Hadamard+UOS quantise of K ({w.N}x{w.d}) {t_k:.2f}s, token-axis "
-                   f"quantise of V {t_v:.2f}s, Q quantise of {rows} rows {t_q:.3f}s, PNQ flash attention of "
-                   f"{rows} query rows x {w.N} keys {t_a:.2f}s; extrapolated x{row_blocks:.1f} row blocks "
-                   f"x{w.H * w.B} heads to {total:.0f}s for the full step. NumPy elementwise work is "
-                   f"single-threaded; BLAS matmuls used up to {blas} threads; "
+                   f"quantise of V {t_v:.2f}s, Q quantise of {rows} rows (from row {row_start}) {t_q:.3f}s, "
+                   f"PNQ flash attention of those {rows} query rows x {w.N} keys {t_a:.2f}s; extrapolated "
+                   f"x{row_blocks:.1f} row blocks x{w.H * w.B} heads to {total:.0f}s for the full step. NumPy "
+                   f"elementwise work is single-threaded; BLAS matmuls used up to {blas} threads; "
                    f"host os.cpu_count()={os.cpu_count()}, affinity={len(os.sched_getaffinity(0))}"),
     }
 
@@ -208,6 +260,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize-pass", action="store_true")
+    ap.add_argument("--no-denominators", action="store_true",
+                    help="skip the microbenchmarks behind the measured roofline denominators")
     ap.add_argument("--traffic-probe", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the scale-rule ablation and the other-shape lines")
@@ -268,20 +322,26 @@ def main():
         step()
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ms_step = time_launches(torch, step, args.steps, stream)
+    steps_ms = time_each(torch, step, args.steps, stream)
+    torch.cuda.synchronize()
     t_wall = (time.perf_counter() - t_wall) / args.steps * 1e3
+    ms_step = sum(steps_ms) / len(steps_ms)
     value = w.flops / (ms_step * 1e-3) / 1e12
 
     # dominant kernel alone, same launch configuration
     for _ in range(2):
         attn_only()
-    ms_attn = time_launches(torch, attn_only, args.steps, stream)
+    attn_ms = time_each(torch, attn_only, args.steps, stream)
+    ms_attn = sum(attn_ms) / len(attn_ms)
     achieved = w.flops / (ms_attn * 1e-3) / 1e12
     abytes = attn_algorithmic_bytes(w)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MXFP4_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_MXFP4_TFLOPS, 4), "traffic": read_traffic(abytes),
-                "kernel": "k_attn<d=128, arranged scales, PNQ>", "ms_per_launch": round(ms_attn, 3),
-                "algorithmic_bytes": abytes}
+                "kernel": "k_attn<d=128, arranged scales, PNQ>", "ms_per_launch": spread(attn_ms),
+                "algorithmic_bytes": abytes,
+                "bound_note": ("'mfma' is the metric's denominator (dense fp4 MFMA peak); the SQ counters show the "
+                               "kernel bound by vector-ALU issue of its softmax (exp and fp4 conversion), priced "
+                               "under alu_floor")}
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -292,18 +352,37 @@ def main():
                    "input_dtype": "bf16", "hadamard": True, "rule": "uos", "pnq": True,
                    "kv_tile": mx.mxattn_kv_tile()},
         "pct_of_mxfp4_peak": round(100.0 * value / PEAK_MXFP4_TFLOPS, 2),
+        "step_ms": spread(steps_ms),
         "wall_ms_per_step": round(t_wall, 3),
         "roofline": roofline,
     }
     del qc, qs, kc, ks, vc, vs, ksa, vsa
 
+    if not args.no_denominators:
+        from mxfp4_bit_attention_amd import probes
+        den = probes.measure(torch, dev)
+        result["denominators"] = den
+        mf = den["mfma_fp4_32x32x64"]["TFLOPs"]
+        roofline["peak_measured"] = mf
+        roofline["frac_measured"] = round(achieved / mf, 4)
+        fl = alu_floor(den, w.d)
+        fl["frac"] = round(achieved / fl["peak_TFLOPs"], 4)
+        roofline["alu_floor"] = fl
+
     if not args.no_quantize_pass:
         qw = synth.QUANT_720P
-        x = synth.device_quant_tensor(qw, dev)
+        # the seeded host law, as the whole-tensor parity test draws it
+        xh = synth.quant_tensor_bf16(qw, threads=min(16, len(os.sched_getaffinity(0))))
+        x = torch.from_numpy(xh.view("int16")).view(torch.bfloat16).to(dev)
+        del xh
         qbytes = quant_algorithmic_bytes(qw)
         c = torch.empty((qw.H, qw.N, qw.d // 2), dtype=torch.uint8, device=dev)
         s = torch.empty((qw.H, qw.N, qw.d // 32), dtype=torch.uint8, device=dev)
-        qp = {"workload": qw.name, "algorithmic_bytes": qbytes, "peak_GBs": PEAK_HBM_GBS}
+        qp = {"workload": qw.name, "algorithmic_bytes": qbytes, "peak_GBs": PEAK_HBM_GBS,
+              "input": "seeded host generator (synth.quant_tensor_bf16)"}
+        if "denominators" in result:
+            qp["stream_read_GBs"] = result["denominators"]["hbm"]["read_GBs"]
+            qp["stream_copy_GBs"] = result["denominators"]["hbm"]["copy_GBs"]
         # right after the attention runs the first ~10 ms of quantize launches run ~5%
         # slower: warm the pass up for ~17 ms before timing any rule
         for _ in range(100):
@@ -315,6 +394,8 @@ def main():
             ms = time_launches(torch, fn, max(args.steps, 50), stream)
             gbs = qbytes / (ms * 1e-3) / 1e9
             qp[name] = {"us": round(ms * 1e3, 1), "GBs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            if "stream_copy_GBs" in qp:
+                qp[name]["frac_of_measured_copy"] = round(gbs / qp["stream_copy_GBs"], 4)
         result["quantize_pass"] = qp
         del x, c, s
 
@@ -324,6 +405,11 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
+        hy = synth.HUNYUAN_720P
+        result["cpu_baseline_other"] = {
+            synth.WAN_480P.name: cpu_baseline(synth.WAN_480P, rows=512),
+            hy.name + " (text rows)": cpu_baseline(hy, rows=hy.text_rows, row_start=hy.N - hy.text_rows),
+        }
     print(json.dumps(result), flush=True)
 
 

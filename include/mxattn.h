@@ -27,6 +27,17 @@
  *    a code is sign << 3 | magnitude index into {0, .5, 1, 1.5, 2, 3, 4, 6}.
  *    Scales are E8M0 bytes: value 2^(byte - 127); 0xFF marks a block that held
  *    Inf or NaN (its codes are 0).
+ *  - Non-finite input.  A block holding Inf or NaN is quantised to scale 0xFF
+ *    (NaN, as the OCP MX format reads that byte) with codes 0, and the attention
+ *    treats it as NaN values, as IEEE arithmetic on the dequantised operands would
+ *    (Pith review, Appendix A opening: the conversion routine handles values the
+ *    format cannot hold): such a block in a query row makes that row of O NaN; in
+ *    any key of K, every row of O (every logit with that key is NaN, and so is each
+ *    row's running max); in V (32 tokens of one channel), that channel of O in
+ *    every row.  The P^ dump records every tile of a NaN row as scale 0xFF, codes 0.
+ *    Logits are accumulated in fp32: inputs for which softmax_scale * |q^ . k^|
+ *    exceeds the fp32 range (about 3.4e38; it takes elements of magnitude above
+ *    roughly 1e18) give unspecified results.
  */
 #ifndef MXATTN_H
 #define MXATTN_H
@@ -88,7 +99,11 @@ int64_t mxattn_padded_tokens(int64_t n);
  *             P = mxattn_padded_tokens(rows):
  *             codes  [batch, cols, P/2]      scales [batch, cols, P/32]
  *             (each column's blocks run along rows; rows past `rows` are zeros,
- *             so their blocks get scale 0x00 and codes 0).
+ *             so their blocks get scale 0x00 and codes 0).  P pads to the kv tile
+ *             (mxattn_kv_tile() = 128 keys), not just to the 32-element block:
+ *             this layout is the attention kernel's V^T operand, which it streams
+ *             one kv tile at a time as a contiguous 64-byte run per channel, and
+ *             the whole-tile padding keeps every such run inside the tensor.
  *   rule_kind, qmax   the scale rule (above).
  *   hadamard  if nonzero, each row is first rotated by the orthonormal
  *             Sylvester Hadamard matrix, y = x H / sqrt(cols), computed in

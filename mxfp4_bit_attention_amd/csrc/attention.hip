@@ -49,10 +49,18 @@ __device__ __forceinline__ v16f mma(const v8i& a, const v8i& b, const v16f& c, i
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, OPA, sa, 0, sb);
 }
 
+// NaN-propagating maxima (v_maximum_f32 / v_maximum3_f32): a NaN logit -- which the
+// block-scaled MFMA produces for every product with a block whose E8M0 scale is 0xFF,
+// the quantisers' mark of a block that held Inf or NaN -- makes the row max NaN, so
+// alpha, l and the row's output become NaN as IEEE arithmetic on the dequantised
+// operands would make them.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 // max / sum over lanes l and l ^ 32
 __device__ __forceinline__ float xmax2(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  return vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
 __device__ __forceinline__ float xsum2(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -218,17 +226,15 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
-
 // Max of the 32 values of one block (a = keys 0..15, b = keys 16..31) with a max3 tree.
 __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
   auto x = [&](int k) { return k < 16 ? a[k] : b[k - 16]; };
   float u[10];  // 16 max operations in three levels: 10, 4 and 2
 #pragma unroll
-  for (int i = 0; i < 10; ++i) u[i] = fmax3(x(3 * i), x(3 * i + 1), x(3 * i + 2));
-  const float w0 = fmax3(u[0], u[1], u[2]), w1 = fmax3(u[3], u[4], u[5]);
-  const float w2 = fmax3(u[6], u[7], u[8]), w3 = fmax3(u[9], x(30), x(31));
-  return fmaxf(fmax3(w0, w1, w2), w3);
+  for (int i = 0; i < 10; ++i) u[i] = vmax3(x(3 * i), x(3 * i + 1), x(3 * i + 2));
+  const float w0 = vmax3(u[0], u[1], u[2]), w1 = vmax3(u[3], u[4], u[5]);
+  const float w2 = vmax3(u[6], u[7], u[8]), w3 = vmax3(u[9], x(30), x(31));
+  return vmax(vmax3(w0, w1, w2), w3);
 }
 
 // Make the compiler produce these values at this point of the program (and not sink
@@ -252,7 +258,10 @@ __device__ __forceinline__ void interleave_mfma() {
 
 // P~ = exp2(x) of block c (x[2c], x[2c+1]) and its PNQ quantisation: codes pc, scale byte psc.
 // The block max of P~ is exp2 of the block max's argument xm (exactly 1 in the row max's block).
-template <bool PNQ>
+// In a row whose running max is NaN the block's P~ are NaN; the P^ dump then records such a
+// block as the quantiser records a non-finite block (scale 0xFF, codes 0), and that scale
+// keeps the block's MFMAs NaN.  Without the dump the row's l is NaN anyway.
+template <bool PNQ, bool DUMP>
 __device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float xm, Rule prule, uint32_t (&pc)[4],
                                          int& psc, float& ls) {
   float p[32];
@@ -264,6 +273,12 @@ __device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float x
   const float pm = __builtin_amdgcn_exp2f(xm);
   psc = mx_scale_byte(__float_as_uint(pm), prule);
   quant32(p, psc, pc);
+  if constexpr (DUMP) {
+    if (__builtin_isnan(pm)) {
+      psc = 0xFF;
+      pc[0] = pc[1] = pc[2] = pc[3] = 0u;
+    }
+  }
   if constexpr (!PNQ) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) ls += p[k];
@@ -363,7 +378,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   }
   const float bm0 = max32(x[0], x[1]);
   const float bm1 = max32(x[2], x[3]);
-  const float mnew = fmaxf(m, xmax2(fmaxf(bm0, bm1)));
+  const float mnew = vmax(m, xmax2(vmax(bm0, bm1)));
   const float alpha = __builtin_amdgcn_exp2f((m - mnew) * cl);
   m = mnew;
   const float mc = mnew * cl;
@@ -400,7 +415,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   uint32_t pc0[4], pc1[4];
   int psc0, psc1;
   float ls = 0.0f;
-  soft_exp<PNQ>(x[0], x[1], xm0, prule, pc0, psc0, ls);
+  soft_exp<PNQ, DUMP>(x[0], x[1], xm0, prule, pc0, psc0, ls);
 
   // rescale the running state when any row's max moved (alpha == 1 is exact)
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -410,7 +425,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   __builtin_amdgcn_sched_barrier(0);
   float r0 = 0.0f, r1 = 0.0f;
   pv_chunk<D, PNQ>(acc, st, lane, vsw[0], 0, ones, pc0, psc0, r0);
-  soft_exp<PNQ>(x[2], x[3], xm1, prule, pc1, psc1, ls);
+  soft_exp<PNQ, DUMP>(x[2], x[3], xm1, prule, pc1, psc1, ls);
   interleave_mfma<NCT + (PNQ ? 1 : 0), 6>();
   __builtin_amdgcn_sched_barrier(0);
   pv_chunk<D, PNQ>(acc, st, lane, vsw[1], 1, ones, pc1, psc1, r1);
@@ -504,8 +519,7 @@ __device__ __forceinline__ void quantise_q_blocks(const AttnArgs& a, int64_t row
   }
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    // integer max of |bits| (this file is built assuming no NaNs, so no float max here):
-    // NaN and Inf sort above every finite value
+    // integer max of |bits|: NaN and Inf sort above every finite value
     uint32_t mb = 0;
 #pragma unroll
     for (int k = 0; k < 32; ++k) mb = max(mb, __float_as_uint(v[s][k]) & 0x7FFFFFFFu);

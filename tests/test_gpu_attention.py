@@ -80,6 +80,29 @@ def test_quantized_entry_p_codes(rule, Nq, Nkv, d):
     assert mm < P_MISMATCH, f"P^ code mismatch {mm:.2e}"
 
 
+@pytest.mark.parametrize("rule", ["uos", "ocp"])
+@pytest.mark.parametrize("Nq,Nkv,d", [(300, 1000, 128), (64, 33, 64), (129, 4096, 128)])
+def test_direct_placement_p_codes(rule, Nq, Nkv, d):
+    """pnq = False (the direct placement of Figure 4(C): l sums the unquantised P~, O~
+    uses P^): the dumped P^ codes and O against the oracle's direct-placement arm."""
+    torch, mx = require_gpu()
+    rng = np.random.default_rng(Nq * 13 + Nkv + d)
+    Q = rng.standard_normal((Nq, d)).astype(np.float32) * 1.5
+    K = rng.standard_normal((Nkv, d)).astype(np.float32) * 1.5
+    V = rng.standard_normal((Nkv, d)).astype(np.float32)
+    Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(Nkv)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    q = _oracle_inputs(Q, K, V, RULES[rule][1], True, P)
+    O, pc, ps = mx.mxattn_forward_quantized(*_device_quantized(q), Nkv, scale, pnq=False,
+                                            p_rule=RULES[rule][0], dump_p=True)
+    torch.cuda.synchronize()
+    Oo, opc, ops = ora.flash_attention_mx(*q, Nkv, scale, False, RULES[rule][1], Bc, return_p=True)
+    err = rel_l2(O.cpu().numpy()[0, 0], Oo)
+    assert err < REL_L2, f"rel-L2 {err:.2e}"
+    mm = p_code_mismatch(u8(pc)[0, 0], u8(ps)[0, 0], opc, ops, Nkv)
+    assert mm < P_MISMATCH, f"P^ code mismatch {mm:.2e}"
+
+
 @pytest.mark.parametrize("rule", ["oas", "q7.5"])
 @pytest.mark.parametrize("Nq,Nkv,d", [(300, 1000, 128), (64, 33, 64)])
 def test_ablation_rules_p_codes(rule, Nq, Nkv, d):
@@ -310,3 +333,59 @@ def test_arranged_entry_is_bitwise_the_quantized_entry(B, H, Nq, Nkv, d, pnq):
         torch.cuda.synchronize()
         assert torch.isfinite(o1).all()
         assert torch.equal(o1, o2), rule
+
+
+@pytest.mark.parametrize("where", ["q", "k", "v"])
+@pytest.mark.parametrize("entry,dtype", [("forward", "f32"), ("forward", "bf16"), ("quantized", "f32")])
+def test_non_finite_blocks_propagate_like_the_oracle(where, entry, dtype):
+    """A 32-element block holding Inf or NaN is quantised to scale 0xFF (NaN), codes 0
+    (Pith review, Axiom ledger axiom 1; Appendix A opening leaves such values to the
+    conversion routine).  The oracle, doing IEEE arithmetic on the dequantised operands,
+    makes NaN exactly the outputs such a block reaches: a query row's block -> that row;
+    a key's block -> every row of the head; a V block (32 tokens of one channel) -> that
+    channel in every row.  The GPU must give the same NaN pattern, match the oracle
+    everywhere else, and (quantised entry) dump the same P^ codes, NaN rows as 0xFF."""
+    torch, mx = require_gpu()
+    rng = np.random.default_rng({"q": 1, "k": 2, "v": 3}[where])
+    B, H, Nq, Nkv, d = 1, 2, 200, 300, 128
+    Q = rng.standard_normal((B, H, Nq, d)).astype(np.float32)
+    K = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, H, Nkv, d)).astype(np.float32)
+    if dtype == "bf16":
+        Q, K, V = (synth.bf16_to_f32(synth.round_to_bf16(a)) for a in (Q, K, V))
+    if where == "q":
+        Q[0, 1, 37, 5] = np.nan
+    elif where == "k":
+        K[0, 0, 250, 70] = np.inf                 # head 0 only: head 1 stays finite
+    else:
+        V[0, 1, 100, 17] = -np.inf
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(Nkv)
+    with np.errstate(invalid="ignore", over="ignore"):
+        if entry == "forward":
+            O = mx.mxattn_forward(*(to_device(a, dtype) for a in (Q, K, V)), scale, hadamard=True, pnq=True,
+                                  rule="uos")
+            torch.cuda.synchronize()
+            Og = O.float().cpu().numpy()
+            Oo = np.stack([ora.mx_attention_pipeline(Q[0, h], K[0, h], V[0, h], scale, True, True, mxfp4.UOS, Bc, P)
+                           for h in range(H)])[None]
+        else:
+            qs = [_oracle_inputs(Q[0, h], K[0, h], V[0, h], mxfp4.UOS, True, P) for h in range(H)]
+            dev = [torch.cat([_device_quantized(q)[i] for q in qs], dim=1) for i in range(6)]
+            O, pc, ps = mx.mxattn_forward_quantized(*dev, Nkv, scale, pnq=True, p_rule="uos", dump_p=True)
+            torch.cuda.synchronize()
+            Og = O.cpu().numpy()
+            res = [ora.flash_attention_mx(*q, Nkv, scale, True, mxfp4.UOS, Bc, return_p=True) for q in qs]
+            Oo = np.stack([r[0] for r in res])[None]
+            for h in range(H):
+                mm = p_code_mismatch(u8(pc)[0, h], u8(ps)[0, h], res[h][1], res[h][2], Nkv)
+                assert mm < P_MISMATCH, f"head {h}: P^ code mismatch {mm:.2e}"
+    nan_o = np.isnan(Oo)
+    expect = {"q": (0, 1, [37], slice(None)), "k": (0, 0, slice(None), slice(None)), "v": (0, 1, slice(None), [17])}
+    b, h, rows, cols = expect[where]
+    assert nan_o[b, h][rows][:, cols].all()           # the oracle's own reading, checked first
+    assert nan_o.sum() == nan_o[b, h][rows][:, cols].size
+    assert np.array_equal(np.isnan(Og), nan_o), f"NaN pattern differs: {np.argwhere(np.isnan(Og) != nan_o)[:4]}"
+    fin = ~nan_o
+    err = rel_l2(Og[fin], Oo[fin])
+    assert err < REL_L2, f"finite outputs: rel-L2 {err:.2e}"
