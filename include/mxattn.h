@@ -231,6 +231,27 @@ int mxattn_forward_arranged(const uint8_t* Qc, const uint8_t* Qs,
                             int32_t p_rule_kind, float p_qmax,
                             void* O, int32_t out_dtype, void* stream);
 
+/*
+ * mxattn_forward_noalloc -- mxattn_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same arguments as mxattn_forward without the workspace, the same
+ * kernels and bitwise the same O; the workspace is a device array inside the library
+ * of MXATTN_NOALLOC_SCRATCH_BYTES.  The call allocates nothing.  Each GPU it runs on
+ * holds its own copy of the array until the process ends; the copy's address is
+ * looked up once per device, on the first call made with that device current.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (different streams, or different host threads) race, so serialise them.
+ * Returns MXATTN_E_WORKSPACE, before any HIP call, when the call needs more than the
+ * array holds (mxattn_forward_workspace_bytes(B, H, Nq, Nkv, d) > the size): at
+ * d = 128 that is about 144 bytes per key per head, so 40 heads of up to about
+ * 46,000 keys fit (Wan2.2-480p's 32,760 do, Wan2.2-720p's 75,600 do not).
+ */
+#define MXATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int mxattn_forward_noalloc(const void* Q, const void* K, const void* V, int32_t dtype,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d,
+                           float softmax_scale, uint32_t hadamard, uint32_t pnq,
+                           int32_t rule_kind, float qmax, void* O, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* mxattn_last_error(void);
 

@@ -8,7 +8,7 @@ module raises if it is missing, and nothing here falls back to a CPU path.
 
 Names mirror the C entry points: ``mxattn_quantize``, ``mxattn_quant_error``, ``mxattn_forward``,
 ``mxattn_forward_quantized``, ``mxattn_arrange_scales``, ``mxattn_forward_arranged``,
-``mxattn_forward_workspace_bytes``,
+``mxattn_forward_noalloc``, ``mxattn_forward_workspace_bytes``,
 ``mxattn_kv_tile``, ``mxattn_padded_tokens``, ``mxattn_last_error``.
 Rules are given as ``"uos"``, ``"ocp"`` or ``("ceil", q)``.
 """
@@ -32,8 +32,10 @@ MXATTN_AXIS_LAST, MXATTN_AXIS_ROWS = 0, 1
 EXPORTED = (
     "mxattn_kv_tile", "mxattn_padded_tokens", "mxattn_quantize", "mxattn_forward_workspace_bytes",
     "mxattn_forward", "mxattn_forward_quantized", "mxattn_last_error", "mxattn_quant_error",
-    "mxattn_arrange_scales", "mxattn_forward_arranged",
+    "mxattn_arrange_scales", "mxattn_forward_arranged", "mxattn_forward_noalloc",
 )
+# bytes of the library's own workspace array behind mxattn_forward_noalloc
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class MxattnError(RuntimeError):
@@ -68,6 +70,8 @@ def _load() -> ctypes.CDLL:
                                              i32, f32, vp, i32, vp, vp, vp]
     lib.mxattn_arrange_scales.restype = c.c_int
     lib.mxattn_arrange_scales.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp]
+    lib.mxattn_forward_noalloc.restype = c.c_int
+    lib.mxattn_forward_noalloc.argtypes = [vp, vp, vp, i32, i64, i64, i64, i64, i64, f32, u32, u32, i32, f32, vp, vp]
     lib.mxattn_forward_arranged.restype = c.c_int
     lib.mxattn_forward_arranged.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, u32, i32, f32,
                                             vp, i32, vp]
@@ -277,6 +281,27 @@ def mxattn_forward(q, k, v, softmax_scale: float, hadamard: bool = True, pnq: bo
     _check(LIB.mxattn_forward(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, Nq, Nkv, d,
                               float(softmax_scale), int(bool(hadamard)), int(bool(pnq)), kind, qm,
                               _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)))
+    return out
+
+
+def mxattn_forward_noalloc(q, k, v, softmax_scale: float, out, hadamard: bool = True, pnq: bool = True,
+                           rule="uos"):
+    """mxattn_forward with the library's own workspace array: nothing is allocated on the
+    device (the caller supplies out [B,H,Nq,d] in q's dtype).  Calls that overlap in time on
+    one GPU share that array and race."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    B, H, Nq, d = q.shape
+    Nkv = k.shape[2]
+    _expect(q, "q", q.shape, _float_dtypes())
+    _expect(k, "k", (B, H, Nkv, d), (q.dtype,))
+    _expect(v, "v", (B, H, Nkv, d), (q.dtype,))
+    _expect(out, "out", (B, H, Nq, d), (q.dtype,))
+    _on_device(q.device, q=q, k=k, v=v, out=out)
+    kind, qm = rule_args(rule)
+    _check(LIB.mxattn_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), B, H, Nq, Nkv, d,
+                                      float(softmax_scale), int(bool(hadamard)), int(bool(pnq)), kind, qm,
+                                      _ptr(out), _stream(q.device)))
     return out
 
 

@@ -27,7 +27,7 @@ LIB = os.path.join(HERE, "libmxattn.so")
 # the attention library itself
 PROBES_LIB = os.path.join(HERE, "libmxattn_probes.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["quantize.hip", "attention.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "attention.hip", "api.cpp", "noalloc.hip"]
 PROBE_SOURCES = ["probes.hip"]
 # Per-source flags beyond the common ones (none at present: every kernel honours NaN,
 # since a non-finite block must turn the outputs it reaches into NaN).

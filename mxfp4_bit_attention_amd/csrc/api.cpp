@@ -315,25 +315,61 @@ int mxattn_forward_arranged(const uint8_t* Qc, const uint8_t* Qs, const uint8_t*
                         nullptr, nullptr, static_cast<hipStream_t>(stream), who, nullptr, Ksa, VTsa);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Every check of mxattn_forward except those of the workspace: dtype, pointers, shape,
+// rule, and the workspace layout the call needs (L).
+int forward_checks(const void* Q, const void* K, const void* V, int32_t dtype, int64_t B, int64_t H, int64_t Nq,
+                   int64_t Nkv, int64_t d, float softmax_scale, int32_t rule_kind, float qmax, const void* O,
+                   const char* who, mxattn::Rule* rule, FwdLayout* L) {
+  if (!elem_bytes(dtype)) return fail(MXATTN_E_INVALID, "%s: dtype must be MXATTN_F32 or MXATTN_BF16", who);
+  if (!Q || !K || !V || !O) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  if (int st = check_attn_shape(B, H, Nq, Nkv, d, softmax_scale, who)) return st;
+  if (int st = make_rule(rule_kind, qmax, rule, who)) return st;
+  if (!fwd_layout(B, H, Nq, Nkv, d, L)) return fail(MXATTN_E_INVALID, "%s: tensor too large", who);
+  return MXATTN_OK;
+}
+
+}  // namespace
+
+namespace mxattn {
+
+int forward_arg_check(const void* Q, const void* K, const void* V, int32_t dtype, int64_t B, int64_t H, int64_t Nq,
+                      int64_t Nkv, int64_t d, float softmax_scale, int32_t rule_kind, float qmax, const void* O,
+                      const char* who, size_t* workspace_bytes) {
+  Rule rule{};
+  FwdLayout L;
+  if (int st = forward_checks(Q, K, V, dtype, B, H, Nq, Nkv, d, softmax_scale, rule_kind, qmax, O, who, &rule, &L))
+    return st;
+  *workspace_bytes = L.total;
+  return MXATTN_OK;
+}
+
+int set_error(int status, const char* message) { return fail(status, "%s", message); }
+
+}  // namespace mxattn
+
+extern "C" {
+
 int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, int64_t B, int64_t H,
                    int64_t Nq, int64_t Nkv, int64_t d, float softmax_scale, uint32_t hadamard,
                    uint32_t pnq, int32_t rule_kind, float qmax, void* O, void* workspace,
                    size_t workspace_bytes, void* stream) {
   const char* who = "mxattn_forward";
-  const int eb = elem_bytes(dtype);
-  if (!eb) return fail(MXATTN_E_INVALID, "%s: dtype must be MXATTN_F32 or MXATTN_BF16", who);
-  if (!Q || !K || !V || !O || !workspace) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
-    return fail(MXATTN_E_INVALID, "%s: pointers must be 16-byte aligned", who);
+  mxattn::Rule rule{};
+  FwdLayout L;
+  if (int st = forward_checks(Q, K, V, dtype, B, H, Nq, Nkv, d, softmax_scale, rule_kind, qmax, O, who, &rule, &L))
+    return st;
+  if (!workspace) return fail(MXATTN_E_INVALID, "%s: null pointer", who);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(MXATTN_E_INVALID, "%s: workspace must be 256-byte aligned", who);
-  if (int st = check_attn_shape(B, H, Nq, Nkv, d, softmax_scale, who)) return st;
-  mxattn::Rule rule{};
-  if (int st = make_rule(rule_kind, qmax, &rule, who)) return st;
-  FwdLayout L;
-  if (!fwd_layout(B, H, Nq, Nkv, d, &L)) return fail(MXATTN_E_INVALID, "%s: tensor too large", who);
   if (workspace_bytes < L.total)
     return fail(MXATTN_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, workspace_bytes, L.total);
+  const int eb = elem_bytes(dtype);
   uint8_t* w = static_cast<uint8_t*>(workspace);
   uint8_t *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs, *ksa = w + L.ksa, *vsa = w + L.vsa;
   hipStream_t s = static_cast<hipStream_t>(stream);

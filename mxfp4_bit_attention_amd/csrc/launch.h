@@ -66,4 +66,13 @@ hipError_t launch_arrange_scales(const uint8_t* ks, const uint8_t* vs, int64_t h
 
 constexpr int kKvTile = 128;
 
+// The argument checks of mxattn_forward other than those of its workspace, with `who`
+// naming the entry point in the error message; on success *workspace_bytes is the
+// workspace the call needs.  Returns MXATTN_OK or the negative status (message set).
+int forward_arg_check(const void* Q, const void* K, const void* V, int32_t dtype, int64_t B, int64_t H, int64_t Nq,
+                      int64_t Nkv, int64_t d, float softmax_scale, int32_t rule_kind, float qmax, const void* O,
+                      const char* who, size_t* workspace_bytes);
+// Sets the thread's mxattn_last_error() message; returns `status`.
+int set_error(int status, const char* message);
+
 }  // namespace mxattn

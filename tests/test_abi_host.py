@@ -197,3 +197,34 @@ def test_binding_rule_parsing(mx):
     assert mx.rule_args(("ceil", 6.0)) == (2, 6.0)
     with pytest.raises(ValueError):
         mx.rule_args("nearest")
+
+
+def n_call(mx, Q=FAKE, dtype=1, B=1, H=2, Nq=256, Nkv=256, d=128, scale=0.125, kind=0, qmax=0.0, O=FAKE):
+    p = ctypes.c_void_p
+    return mx.LIB.mxattn_forward_noalloc(p(Q), p(FAKE), p(FAKE), dtype, B, H, Nq, Nkv, d, scale, 1, 1, kind,
+                                         qmax, p(O), None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(Q=0), -1, "null"),
+    (dict(O=MISALIGNED), -1, "aligned"),
+    (dict(d=96), -2, "64 or 128"),
+    (dict(scale=0.0), -1, "softmax_scale"),
+    (dict(kind=2, qmax=9.0), -1, "(4, 8]"),
+    # 40 heads x 75,600 keys at d = 128 need about 435 MB of workspace: beyond the array
+    (dict(H=40, Nq=75600, Nkv=75600), -3, "bytes of scratch"),
+])
+def test_forward_noalloc_rejects_before_any_hip_call(mx, kw, status, msg):
+    """Every rejection of the allocation-free forward happens on the host, before the
+    library's array is looked up or anything is launched (so these run without a GPU)."""
+    assert n_call(mx, **kw) == status
+    assert msg in mx.mxattn_last_error() and "mxattn_forward_noalloc" in mx.mxattn_last_error()
+
+
+def test_forward_noalloc_size_limit_matches_the_workspace_size(mx):
+    """The largest call the array admits is the one whose mxattn_forward workspace fits in it."""
+    limit = mx.NOALLOC_SCRATCH_BYTES
+    assert mx.mxattn_forward_workspace_bytes(1, 40, 32760, 32760, 128) <= limit       # Wan2.2-480p fits
+    assert mx.mxattn_forward_workspace_bytes(1, 40, 75600, 75600, 128) > limit        # Wan2.2-720p does not
+    src = open(HEADER).read()
+    assert "#define MXATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)" in src and limit == 256 << 20
