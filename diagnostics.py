@@ -1,4 +1,5 @@
-"""Mechanism diagnostics of MXFP4 scale rules on the GPU (through the C ABI).
+#!/usr/bin/env python3
+"""Mechanism diagnostics of MXFP4 scale rules on the GPU (a study script, like bench.py).
 
 The Pith review's referee report notes that the optimality of the UOS constant
 q = 7.25 is argued for a model density of block maxima, and that per-block Qmax
@@ -18,14 +19,24 @@ those sweeps on any tensor with the library's own kernels:
                                 quantised tile for each g, and the g that brings their
                                 average closest to one (Figure 7, panel C).
 
-Quantisation and attention run in libmxattn; torch only reduces the results.
+Quantisation and attention run in libmxattn through the binding; the references these
+studies compare against (softmax on dequantised operands, a replay of the unquantised
+P~, row sums) are reductions in torch here, outside the product package, which holds
+only the binding of the HIP path.
+
+    python diagnostics.py          (one JSON line on the Wan2.2-720p-shaped tensors)
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import (mxattn_forward_quantized, mxattn_kv_tile, mxattn_padded_tokens, mxattn_quant_error,
-               mxattn_quantize)
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+from mxfp4_bit_attention_amd import (mxattn_forward_quantized, mxattn_kv_tile,  # noqa: E402
+                                     mxattn_padded_tokens, mxattn_quant_error, mxattn_quantize)
 
 SWEEP_QS = tuple(round(6.0 + 0.05 * i, 2) for i in range(41))  # 6.00, 6.05, ..., 8.00
 
@@ -198,10 +209,7 @@ def main() -> None:
     decomposition on the first 8192 tokens of head 0 (512 rows), and the global-scaling arm
     on 256 rows of head 0's materialised P (all 75,600 keys)."""
     import json
-    import os
-    import sys
     import torch
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     import synth
     w = synth.WAN_720P
     dev = torch.device("cuda:0")

@@ -254,6 +254,10 @@ static int attention_core(const uint8_t* Qc, const uint8_t* Qs, const uint8_t* K
   a.kv_pad = round_up(Nkv, mxattn::kKvTile);
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   a.out_bf16 = out_dtype == MXATTN_BF16;
+  // the P~ rule for the kernel's log-domain block exponent (Rule's OCP encoding has a
+  // fraction threshold no fraction exceeds; CEIL(q) has q = (1 + q_frac / 2^23) 2^q_exp)
+  a.p_floor = pr.q_frac > 0x7FFFFFu ? 1 : 0;
+  a.p_log2q = a.p_floor ? 0.0f : (float)std::log2(std::ldexp(1.0 + pr.q_frac / 8388608.0, pr.q_exp));
   if (fused) {
     a.qraw = fused->q;
     a.q_bf16 = fused->bf16 ? 1 : 0;

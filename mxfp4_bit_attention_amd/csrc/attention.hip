@@ -256,25 +256,41 @@ __device__ __forceinline__ void interleave_mfma() {
   }
 }
 
+// Scale operand 2^e of the fp4 conversion for one P~ block, from y: the log2 of the
+// block's largest P~ minus log2 q under CEIL(q) (the smallest e with max P~ <= q 2^e is
+// ceil(y)), or that log2 itself under the OCP floor rule (e = floor(y) - 2).  Deciding in
+// the log domain takes no exponential; it agrees with the decision on the fp32 value of
+// max P~ except within a few fp32 ulps of a boundary.  v_ldexp_f32 makes 2^e subnormal or
+// zero for e < -126, whose exponent field 0 is the E8M0 byte that clamps every e <= -127
+// (the conversion reads only that field, as 2^-127).
+template <bool PFLOOR>
+__device__ __forceinline__ float p_block_scale(float y) {
+  const float t = PFLOOR ? __builtin_floorf(y) : __builtin_ceilf(y);
+  int e;
+  asm("v_cvt_i32_f32 %0, %1" : "=v"(e) : "v"(t));  // saturating: -inf -> INT_MIN, NaN -> 0
+  return __builtin_amdgcn_ldexpf(PFLOOR ? 0.25f : 1.0f, e);
+}
+
 // P~ = exp2(x) of block c (x[2c], x[2c+1]) and its PNQ quantisation: codes pc, scale byte psc.
-// The block max of P~ is exp2 of the block max's argument xm (exactly 1 in the row max's block).
+// y is the block's scale argument (p_block_scale); in the block that holds the row max the
+// largest P~ is exactly 1 and y is exactly -log2 q (CEIL) or 0 (OCP).
 // In a row whose running max is NaN the block's P~ are NaN; the P^ dump then records such a
 // block as the quantiser records a non-finite block (scale 0xFF, codes 0), and that scale
 // keeps the block's MFMAs NaN.  Without the dump the row's l is NaN anyway.
-template <bool PNQ, bool DUMP>
-__device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float xm, Rule prule, uint32_t (&pc)[4],
-                                         int& psc, float& ls) {
+template <bool PNQ, bool DUMP, bool PFLOOR>
+__device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float y, uint32_t (&pc)[4], int& psc,
+                                         float& ls) {
   float p[32];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     p[k] = __builtin_amdgcn_exp2f(xa[k]);
     p[16 + k] = __builtin_amdgcn_exp2f(xb[k]);
   }
-  const float pm = __builtin_amdgcn_exp2f(xm);
-  psc = mx_scale_byte(__float_as_uint(pm), prule);
-  quant32(p, psc, pc);
+  const float sc = p_block_scale<PFLOOR>(y);
+  psc = (int)(__float_as_uint(sc) >> 23);
+  quant_pairs(p, sc, pc);
   if constexpr (DUMP) {
-    if (__builtin_isnan(pm)) {
+    if (__builtin_isnan(y)) {
       psc = 0xFF;
       pc[0] = pc[1] = pc[2] = pc[3] = 0u;
     }
@@ -312,10 +328,10 @@ __device__ __forceinline__ void pv_chunk(v16f (&acc)[D / 32], const uint8_t* __r
 
 // One kv tile for one wave's 32 queries.  `rem` (TAIL only) is the number of valid
 // keys in the tile.
-template <int D, bool PRE, bool PNQ, bool DUMP, bool TAIL>
+template <int D, bool PRE, bool PNQ, bool DUMP, bool PFLOOR, bool TAIL>
 __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int lane, Sel sel0, Sel sel1, int rem,
                                             const v8i (&qf)[D / 64], const int (&qsc)[D / 64],
-                                            v16f (&acc)[D / 32], float& m, float& l, float cl, Rule prule,
+                                            v16f (&acc)[D / 32], float& m, float& l, float cl, float plq,
                                             const AttnArgs& a, int64_t qrow, int64_t head, int j,
                                             const uint32_t* lones) {
   using G = Geo<D>;
@@ -386,10 +402,11 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int v = 0; v < 16; ++v) x[t][v] = __builtin_fmaf(x[t][v], cl, -mc);
-  // the block maxes' arguments as a difference first: exactly 0 in the block that holds
-  // the row max, whose P~ block max is then exactly 1 as the method defines it (an fma
-  // here can leave a rounding residue and move the floor rule's exponent)
-  const float xm0 = (bm0 - mnew) * cl, xm1 = (bm1 - mnew) * cl;
+  // the blocks' scale arguments from a difference first: exactly 0 in the block that
+  // holds the row max, whose P~ block max is then exactly 1 as the method defines it (an
+  // fma of bm alone can leave a rounding residue and move the exponent)
+  const float y0 = PFLOOR ? (bm0 - mnew) * cl : __builtin_fmaf(bm0 - mnew, cl, -plq);
+  const float y1 = PFLOOR ? (bm1 - mnew) * cl : __builtin_fmaf(bm1 - mnew, cl, -plq);
 
   // V^ scales (the fragments are read per chunk in pv_chunk)
   int vsw[2];
@@ -415,7 +432,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   uint32_t pc0[4], pc1[4];
   int psc0, psc1;
   float ls = 0.0f;
-  soft_exp<PNQ, DUMP>(x[0], x[1], xm0, prule, pc0, psc0, ls);
+  soft_exp<PNQ, DUMP, PFLOOR>(x[0], x[1], y0, pc0, psc0, ls);
 
   // rescale the running state when any row's max moved (alpha == 1 is exact)
   if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
@@ -425,7 +442,7 @@ __device__ __forceinline__ void attend_tile(const uint8_t* __restrict__ st, int 
   __builtin_amdgcn_sched_barrier(0);
   float r0 = 0.0f, r1 = 0.0f;
   pv_chunk<D, PNQ>(acc, st, lane, vsw[0], 0, ones, pc0, psc0, r0);
-  soft_exp<PNQ, DUMP>(x[2], x[3], xm1, prule, pc1, psc1, ls);
+  soft_exp<PNQ, DUMP, PFLOOR>(x[2], x[3], y1, pc1, psc1, ls);
   interleave_mfma<NCT + (PNQ ? 1 : 0), 6>();
   __builtin_amdgcn_sched_barrier(0);
   pv_chunk<D, PNQ>(acc, st, lane, vsw[1], 1, ones, pc1, psc1, r1);
@@ -534,7 +551,7 @@ __device__ __forceinline__ void quantise_q_blocks(const AttnArgs& a, int64_t row
 }
 
 // One workgroup = NW waves of 32 queries.
-template <int D, bool PRE, bool PNQ, bool DUMP>
+template <int D, bool PRE, bool PNQ, bool DUMP, bool PFLOOR>
 __global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtiles, int nblocks) {
   using G = Geo<D>;
   constexpr int S = G::S;
@@ -637,12 +654,14 @@ __global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtil
   int j = 0;
   for (; j < nfull; ++j) {
     const uint8_t* cur = enter(j);
-    attend_tile<D, PRE, PNQ, DUMP, false>(cur, lane, sel0, sel1, BC, qf, qsc, acc, m, l, cl, prule, a, qrow, head, j,
+    attend_tile<D, PRE, PNQ, DUMP, PFLOOR, false>(cur, lane, sel0, sel1, BC, qf, qsc, acc, m, l, cl, a.p_log2q, a, qrow,
+                                                  head, j,
                                      lones);
   }
   if (j < ntiles) {  // the ragged last tile, masked
     const uint8_t* cur = enter(j);
-    attend_tile<D, PRE, PNQ, DUMP, true>(cur, lane, sel0, sel1, nkv - j * BC, qf, qsc, acc, m, l, cl, prule, a, qrow,
+    attend_tile<D, PRE, PNQ, DUMP, PFLOOR, true>(cur, lane, sel0, sel1, nkv - j * BC, qf, qsc, acc, m, l, cl, a.p_log2q,
+                                                 a, qrow,
                                     head, j, lones);
   }
   MX_VMCNT(0);  // no DMA may still target this workgroup's LDS when it exits
@@ -675,28 +694,30 @@ __global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtil
   }
 }
 
+template <int D, bool PRE, bool PNQ, bool DUMP>
+static void launch_rule(const AttnArgs& a, Rule pr, dim3 grid, int qtiles, int nblocks, hipStream_t s) {
+  if (a.p_floor)
+    hipLaunchKernelGGL((k_attn<D, PRE, PNQ, DUMP, true>), grid, dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  else
+    hipLaunchKernelGGL((k_attn<D, PRE, PNQ, DUMP, false>), grid, dim3(NT), 0, s, a, pr, qtiles, nblocks);
+}
+
 template <int D>
 static hipError_t launch_d(const AttnArgs& a, int pnq, Rule pr, hipStream_t s) {
   const int qtiles = (int)((a.nq + BR - 1) / BR);
   const int64_t nb = (int64_t)qtiles * a.heads;
   if (nb > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
   const int nblocks = (int)nb;
-  const unsigned grid = (unsigned)((nblocks + 7) / 8 * 8);
+  const dim3 grid((unsigned)((nblocks + 7) / 8 * 8));
   const bool dump = a.pc != nullptr;
   const bool pre = a.ksa != nullptr;
   if (pre && dump) return hipErrorInvalidValue;  // the P^ dump comes with caller-layout operands only
-  if (pre && pnq)
-    hipLaunchKernelGGL((k_attn<D, true, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
-  else if (pre)
-    hipLaunchKernelGGL((k_attn<D, true, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
-  else if (pnq && !dump)
-    hipLaunchKernelGGL((k_attn<D, false, true, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
-  else if (pnq && dump)
-    hipLaunchKernelGGL((k_attn<D, false, true, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
-  else if (!dump)
-    hipLaunchKernelGGL((k_attn<D, false, false, false>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
-  else
-    hipLaunchKernelGGL((k_attn<D, false, false, true>), dim3(grid), dim3(NT), 0, s, a, pr, qtiles, nblocks);
+  if (pre && pnq) launch_rule<D, true, true, false>(a, pr, grid, qtiles, nblocks, s);
+  else if (pre) launch_rule<D, true, false, false>(a, pr, grid, qtiles, nblocks, s);
+  else if (pnq && !dump) launch_rule<D, false, true, false>(a, pr, grid, qtiles, nblocks, s);
+  else if (pnq && dump) launch_rule<D, false, true, true>(a, pr, grid, qtiles, nblocks, s);
+  else if (!dump) launch_rule<D, false, false, false>(a, pr, grid, qtiles, nblocks, s);
+  else launch_rule<D, false, false, true>(a, pr, grid, qtiles, nblocks, s);
   return hipGetLastError();
 }
 

@@ -56,6 +56,10 @@ struct AttnArgs {
   int q_bf16;
   int q_hadamard;
   float q_c;  // fl32(1/sqrt(d)), the rotation's final multiplier
+  // The P~ rule in the attention kernel's log-domain form: the OCP floor rule
+  // (p_floor = 1), or CEIL(q) with p_log2q = fl32(log2 q).
+  int p_floor;
+  float p_log2q;
 };
 
 hipError_t launch_attention(const AttnArgs& a, int d, int pnq, Rule p_rule, hipStream_t s);

@@ -45,10 +45,9 @@ __device__ __forceinline__ uint32_t cvt_pk_fp4(uint32_t old, float a, float b, f
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
-// Quantise 32 fp32 values v[0..31] with scale byte eb (any eb in [0, 254]) into
-// 4 dwords of codes, element k in nibble k of the 16 bytes.
-__device__ __forceinline__ void quant32(const float* v, int eb, uint32_t out[4]) {
-  const float s = e8m0_scale(eb);
+// Quantise 32 fp32 values v[0..31] with the conversion's scale operand s (an fp32 whose
+// exponent field is the E8M0 byte) into 4 dwords of codes, element k in nibble k.
+__device__ __forceinline__ void quant_pairs(const float* v, float s, uint32_t out[4]) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     // all four bytes of r are written below, so its initial value is irrelevant:
@@ -61,6 +60,9 @@ __device__ __forceinline__ void quant32(const float* v, int eb, uint32_t out[4])
     out[w] = r;
   }
 }
+
+// The same with scale byte eb (any eb in [0, 254]).
+__device__ __forceinline__ void quant32(const float* v, int eb, uint32_t out[4]) { quant_pairs(v, e8m0_scale(eb), out); }
 
 // Largest |v[i]| of a 32-element block as fp32 bits, with the NaN-propagating
 // maximum (v_maximum3_f32 with |.| operand modifiers): the result, sign cleared,

@@ -1,5 +1,5 @@
 """GPU parity of the scale-rule diagnostics (mxattn_quant_error and the helpers of
-mxfp4_bit_attention_amd.diagnostics) against oracle/diagnostics.py and the oracle's
+diagnostics.py) against oracle/diagnostics.py and the oracle's
 attention.  The quantisers are bit-exact, so the error sums differ from the oracle's
 float64 sums only by the kernel's fp32 per-block accumulation."""
 import numpy as np
@@ -60,7 +60,7 @@ def test_quant_error_counts_nonfinite_blocks():
 
 def test_qmax_sweep_matches_oracle():
     torch, mx = require_gpu()
-    from mxfp4_bit_attention_amd import diagnostics as dg
+    import diagnostics as dg
     x = synth.quant_head(synth.TINY_QUANT, 0)
     qs = (6.0, 6.5, 7.0, 7.25, 7.5, 8.0)
     sw = dg.qmax_sweep(to_device(x, "f32"), qs=qs, hadamard=True)
@@ -73,7 +73,7 @@ def test_qmax_sweep_matches_oracle():
 
 def test_p_tile_sweep_matches_oracle():
     torch, mx = require_gpu()
-    from mxfp4_bit_attention_amd import diagnostics as dg
+    import diagnostics as dg
     w = synth.TINY
     Q, K, V = (synth.attn_head(w, t, 0) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
     scale = float(np.float32(w.softmax_scale))
@@ -95,7 +95,7 @@ def test_p_tile_sweep_matches_oracle():
 @pytest.mark.parametrize("rule", ["uos", "ocp"])
 def test_rowsum_decomposition_matches_oracle(rule):
     torch, mx = require_gpu()
-    from mxfp4_bit_attention_amd import diagnostics as dg
+    import diagnostics as dg
     rng = np.random.default_rng(12)
     n, d = 700, 128
     Q = (rng.standard_normal((n, d)) * 1.5).astype(np.float32)
@@ -117,7 +117,7 @@ def test_global_scaling_matches_oracle(rule):
     oracle's on the same fp32 P (the quantiser is bit-exact; only the float64 summation
     order differs), for a few g and for the g the sweep picks."""
     torch, mx = require_gpu()
-    from mxfp4_bit_attention_amd import diagnostics as dg
+    import diagnostics as dg
     w = synth.TINY
     Q, K, V = (synth.attn_tensor(w, t) for t in (synth.Q_ID, synth.K_ID, synth.V_ID))
     q, k, v = (to_device(x[0, 0], "f32") for x in (Q, K, V))
