@@ -389,3 +389,56 @@ def test_non_finite_blocks_propagate_like_the_oracle(where, entry, dtype):
     fin = ~nan_o
     err = rel_l2(Og[fin], Oo[fin])
     assert err < REL_L2, f"finite outputs: rel-L2 {err:.2e}"
+
+
+@pytest.mark.parametrize("rule", ["uos", "ocp"])
+@pytest.mark.parametrize("Nkv", [1, 77, 300])
+def test_equal_logits_average_v_exactly(rule, Nkv):
+    """Degenerate case of the method: with K = 0 every logit is 0, every P~ = exp(0 - 0)
+    is exactly 1 and (a block of ones quantises exactly under every rule here) every P^ is
+    1, so PNQ's O is the plain average of the dequantised V^ rows, to fp32 rounding of the
+    sums.  Checked against that closed form and against the oracle."""
+    torch, mx = require_gpu()
+    rng = np.random.default_rng(Nkv)
+    Nq, d = 70, 128
+    Q = rng.standard_normal((Nq, d)).astype(np.float32)
+    K = np.zeros((Nkv, d), np.float32)
+    V = rng.standard_normal((Nkv, d)).astype(np.float32)
+    Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(Nkv)
+    q = _oracle_inputs(Q, K, V, RULES[rule][1], True, P)
+    O, pc, ps = mx.mxattn_forward_quantized(*_device_quantized(q), Nkv, 0.125, pnq=True, p_rule=RULES[rule][0],
+                                            dump_p=True)
+    torch.cuda.synchronize()
+    Og = O.cpu().numpy()[0, 0]
+    Vd = mxfp4.dequantize_blocks_lastaxis(q[4], q[5]).T[:Nkv]
+    mean = Vd.mean(axis=0)
+    assert np.abs(Og - mean).max() <= 1e-5 * max(1.0, np.abs(mean).max())
+    Oo, opc, ops = ora.flash_attention_mx(*q, Nkv, 0.125, True, RULES[rule][1], Bc, return_p=True)
+    assert rel_l2(Og, Oo) < 1e-6
+    assert p_code_mismatch(u8(pc)[0, 0], u8(ps)[0, 0], opc, ops, Nkv) == 0.0
+
+
+def test_largest_query_count():
+    """N_q = 2^24, the most query rows per head the ABI accepts (131,072 query tiles in one
+    launch, a 2 GiB bf16 Q), against 300 keys: sampled rows -- the first, the last, both
+    sides of 2^23 and random ones -- against the oracle on the same inputs."""
+    torch, mx = require_gpu()
+    Nq, Nkv, d = 1 << 24, 300, 64
+    g = torch.Generator(device="cuda").manual_seed(24)
+    q = torch.randn((1, 1, Nq, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, 1, Nkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, 1, Nkv, d), generator=g, device="cuda").to(torch.bfloat16)
+    scale = 0.125
+    O = mx.mxattn_forward(q, k, v, scale, hadamard=True, pnq=True, rule="uos")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, (1 << 23) - 1, 1 << 23, Nq - 1],
+                                     np.random.default_rng(24).choice(Nq, 27, replace=False)]))
+    ridx = torch.from_numpy(rows).cuda()
+    Og = O[0, 0, ridx].float().cpu().numpy()
+    Qh = q[0, 0, ridx].float().cpu().numpy()
+    Kh, Vh = k[0, 0].float().cpu().numpy(), v[0, 0].float().cpu().numpy()
+    del q, O
+    Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(Nkv)
+    Oo = ora.mx_attention_pipeline(Qh, Kh, Vh, scale, True, True, mxfp4.UOS, Bc, P)
+    err = rel_l2(Og, Oo)
+    assert err < REL_L2, f"rel-L2 {err:.2e}"
