@@ -28,8 +28,8 @@ Printed as one JSON line, with:
   rule_ablation  the full step under each shared-exponent rule (UOS, OCP, TFS,
                  OAS and CEIL 7.5; the same rule for Q, K, V and P~);
   other_shapes   the full step at d = 64, at B = 2 x H = 20, with 512 keys
-                 (cross-attention-like), and on the Wan2.2-480p and
-                 HunyuanVideo-720p workloads;
+                 (cross-attention-like), at 2,048 / 4,096 / 8,192 tokens, and on
+                 the Wan2.2-480p and HunyuanVideo-720p workloads;
   cpu_baseline   the CPU oracle timed on a bounded sample of the same workload
                  on this host, extrapolated to the full workload (and, under
                  cpu_baseline_other, the same for Wan2.2-480p and for
@@ -232,7 +232,10 @@ def extras(torch, mx, w, q, k, v, out, ws, stream, iters: int = 5) -> dict:
     shapes = {}
     other = (("d64", dict(B=1, H=40, Nq=w.N, Nkv=w.N, d=64)),
              ("B2_H20", dict(B=2, H=20, Nq=w.N, Nkv=w.N, d=128)),
-             ("cross_Nkv512", dict(B=1, H=40, Nq=w.N, Nkv=512, d=128)))
+             ("cross_Nkv512", dict(B=1, H=40, Nq=w.N, Nkv=512, d=128)),
+             ("N2048", dict(B=1, H=40, Nq=2048, Nkv=2048, d=128)),
+             ("N4096", dict(B=1, H=40, Nq=4096, Nkv=4096, d=128)),
+             ("N8192", dict(B=1, H=40, Nq=8192, Nkv=8192, d=128)))
     for name, sh in other:
         g = torch.Generator(device=q.device).manual_seed(7)
         mk = lambda n: torch.randn((sh["B"], sh["H"], n, sh["d"]), generator=g, device=q.device).to(torch.bfloat16)
@@ -243,7 +246,8 @@ def extras(torch, mx, w, q, k, v, out, ws, stream, iters: int = 5) -> dict:
         sc = 1.0 / math.sqrt(sh["d"])
         fn = lambda: mx.mxattn_forward(qq, kk, vv, sc, hadamard=True, pnq=True, rule="uos", out=oo, workspace=wws)
         fn()
-        ms = time_launches(torch, fn, iters, stream)
+        # short steps are timed over more launches so that each timing spans several ms
+        ms = time_launches(torch, fn, iters if sh["Nq"] * sh["Nkv"] > 1 << 26 else 20 * iters, stream)
         flops = 4.0 * sh["B"] * sh["H"] * sh["Nq"] * sh["Nkv"] * sh["d"]
         shapes[name] = dict(sh, ms_per_step=round(ms, 3), TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1))
         del qq, kk, vv, oo, wws

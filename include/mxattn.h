@@ -140,10 +140,11 @@ int mxattn_quant_error(const void* x, int32_t dtype, int64_t batch, int64_t rows
                        int32_t axis, int32_t rule_kind, float qmax, uint32_t hadamard,
                        double* sums, void* stream);
 
-/* Bytes of workspace mxattn_forward needs: the quantised K (along d), the
- * transposed quantised V (along tokens) and both scale sets in the order of
- * mxattn_arrange_scales, each piece 256-byte aligned (Q is rotated and quantised
- * inside the attention kernel and never stored).  Returns 0 for invalid sizes. */
+/* Bytes of workspace mxattn_forward needs: the codes of the quantised K (along d)
+ * and of the transposed quantised V (along tokens), and both scale sets, which the
+ * forward's quantisers write directly in the order of mxattn_arrange_scales; each
+ * piece 256-byte aligned (Q is rotated and quantised inside the attention kernel and
+ * never stored).  Returns 0 for invalid sizes. */
 size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d);
 
 /*
@@ -243,8 +244,8 @@ int mxattn_forward_arranged(const uint8_t* Qc, const uint8_t* Qs,
  * GPU (different streams, or different host threads) race, so serialise them.
  * Returns MXATTN_E_WORKSPACE, before any HIP call, when the call needs more than the
  * array holds (mxattn_forward_workspace_bytes(B, H, Nq, Nkv, d) > the size): at
- * d = 128 that is about 144 bytes per key per head, so 40 heads of up to about
- * 46,000 keys fit (Wan2.2-480p's 32,760 do, Wan2.2-720p's 75,600 do not).
+ * d = 128 that is about 136 bytes per key per head, so 40 heads of up to about
+ * 49,000 keys fit (Wan2.2-480p's 32,760 do, Wan2.2-720p's 75,600 do not).
  */
 #define MXATTN_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
 int mxattn_forward_noalloc(const void* Q, const void* K, const void* V, int32_t dtype,

@@ -95,20 +95,19 @@ struct Carve {
 };
 
 struct FwdLayout {
-  size_t kc, ks, vc, vs, ksa, vsa, total;
+  size_t kc, vc, ksa, vsa, total;
 };
 
-// The forward's workspace: K^ and V^T (Q is quantised inside the attention kernel),
-// and both scale sets re-ordered per kv tile for the attention kernel's lanes.
+// The forward's workspace: the codes of K^ and V^T (Q is quantised inside the attention
+// kernel), and their scales, which the quantisers write straight into the attention
+// kernel's per-tile operand order.
 bool fwd_layout(int64_t B, int64_t H, int64_t Nq, int64_t Nkv, int64_t d, FwdLayout* L) {
   int64_t nq_e, nkv_e, v_e;
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
   if (!elems(B, H, Nq, d, &nq_e) || !elems(B, H, Nkv, d, &nkv_e) || !elems(B, H, P, d, &v_e)) return false;
   Carve c;
   L->kc = c.take((size_t)nkv_e / 2);
-  L->ks = c.take((size_t)nkv_e / 32);
   L->vc = c.take((size_t)v_e / 2);
-  L->vs = c.take((size_t)v_e / 32);
   L->ksa = c.take((size_t)(B * H * P) * 4);
   L->vsa = c.take((size_t)(B * H * P) * 4);
   L->total = c.off;
@@ -375,22 +374,22 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, i
     return fail(MXATTN_E_WORKSPACE, "%s: workspace has %zu bytes, needs %zu", who, workspace_bytes, L.total);
   const int eb = elem_bytes(dtype);
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  uint8_t *kc = w + L.kc, *ks = w + L.ks, *vc = w + L.vc, *vs = w + L.vs, *ksa = w + L.ksa, *vsa = w + L.vsa;
+  uint8_t *kc = w + L.kc, *vc = w + L.vc, *ksa = w + L.ksa, *vsa = w + L.vsa;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
   const float c = inv_sqrt_f32((int)d);
   hipError_t e;
+  // K^ and V^T with their scales already in the attention kernel's operand order
   if (hadamard)
-    e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ks, rule, c, nullptr, s);
+    e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ksa, rule, c, nullptr, s, Nkv, P);
   else
-    e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ks, rule, nullptr, s);
-  if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vs, rule, nullptr, s);
-  if (e == hipSuccess) e = mxattn::launch_arrange_scales(ks, vs, B * H, Nkv, P, (int)d, ksa, vsa, s);
+    e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ksa, rule, nullptr, s, (int)(d / 32), Nkv, P);
+  if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vsa, rule, nullptr, s, true);
   if (e != hipSuccess) return hip_fail(e, who);
   // Q is read once per query tile: the attention kernel rotates and quantises it itself
   const QuantQ fused{Q, eb == 2, hadamard != 0, c};
-  return attention_core(nullptr, nullptr, kc, ks, vc, vs, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O, dtype,
-                        nullptr, nullptr, s, who, &fused, ksa, vsa);
+  return attention_core(nullptr, nullptr, kc, nullptr, vc, nullptr, B, H, Nq, Nkv, d, softmax_scale, pnq, rule, O,
+                        dtype, nullptr, nullptr, s, who, &fused, ksa, vsa);
 }
 
 }  // extern "C"

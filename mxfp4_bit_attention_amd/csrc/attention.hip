@@ -592,6 +592,13 @@ __global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtil
                                     a.vc + head * (int64_t)D * (kvp / 2), a.vs + head * (int64_t)D * (kvp / 32),
                                     nkv * (D / 2), nkv * (D / 32), D * (kvp / 2), D * (kvp / 32)};
 
+  // ---- three-stage ring: tile j lives in stage j % 3; its DMA is issued two tiles
+  // ahead, right after the barrier that retires the reads of the stage it reuses.  The
+  // first two go out before the Q prologue, whose loads and rotation then overlap them.
+  const DmaOffsets<D> dof = dma_offsets<D, PRE>(a.kv_pad, wave, lane);
+  tile_dma<D, PRE>(st0, dof, src, 0, wave, lane);
+  tile_dma<D, PRE>(st1, dof, src, 1, wave, lane);
+
   // ---- Q^ fragments (B operand of S^T), kept for the whole kv loop: lane (i, h) holds
   // blocks 2s + h of query row i.  Either read from the quantised Q^, or made here
   // from the raw query rows (the fused prologue of mxattn_forward).
@@ -628,11 +635,6 @@ __global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtil
   const int ntiles = (nkv + BC - 1) / BC;
   const int nfull = nkv / BC;  // tiles with no padded key
 
-  // ---- three-stage ring: tile j lives in stage j % 3; its DMA is issued two tiles
-  // ahead, right after the barrier that retires the reads of the stage it reuses.
-  const DmaOffsets<D> dof = dma_offsets<D, PRE>(a.kv_pad, wave, lane);
-  tile_dma<D, PRE>(st0, dof, src, 0, wave, lane);
-  tile_dma<D, PRE>(st1, dof, src, 1, wave, lane);
   if (tid < 4) lones[tid] = 0x22222222u;
 
   // Wait for this wave's DMAs of tile j (those of tile j + 1 may stay in flight);

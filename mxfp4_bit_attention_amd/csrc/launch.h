@@ -18,15 +18,24 @@ struct Rule {
 
 // Quantisers.  With err == nullptr they store codes and scales; with err != nullptr
 // they store nothing and add {sum (x - dequant)^2, sum x^2, non-finite blocks} to err[0..2].
+// Scales go to the layout of mxattn_quantize, or -- arr_keys > 0 / arranged, for the
+// forward's own K^ and V^T -- straight into the attention kernel's per-tile operand order
+// (the layout of mxattn_arrange_scales: arr_keys rows per head, 4 arr_pad bytes per head;
+// for V one head per batch item and 4 P bytes).  The arranged bytes of key slots past the
+// last key of a head are not written: the attention kernel masks those keys' logits.
 // Fused Hadamard + quantise along the last axis; d in {64, 128}; eb = 2 (bf16) or 4 (fp32).
 hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, uint8_t* codes,
-                                 uint8_t* scales, Rule rule, float c, double* err, hipStream_t s);
-// Quantise along the last axis in 32-element blocks (nblocks blocks, contiguous).
+                                 uint8_t* scales, Rule rule, float c, double* err, hipStream_t s,
+                                 int64_t arr_keys = 0, int64_t arr_pad = 0);
+// Quantise along the last axis in 32-element blocks (nblocks blocks, contiguous;
+// blocks_per_row of them per row when the scales are arranged).
 hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* codes, uint8_t* scales,
-                             Rule rule, double* err, hipStream_t s);
+                             Rule rule, double* err, hipStream_t s, int blocks_per_row = 0, int64_t arr_keys = 0,
+                             int64_t arr_pad = 0);
 // Quantise down the rows, transposed output with P (multiple of 128) padded tokens.
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
-                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s);
+                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s,
+                             bool arranged = false);
 // Sets n doubles to zero with a kernel (graph-capturable, unlike a memset node).
 hipError_t launch_zero_f64(double* p, int n, hipStream_t s);
 

@@ -84,6 +84,36 @@ __device__ __forceinline__ uint32_t absmax32_bits(const float* v) {
   return __float_as_uint(amax2(amax3(w0, w1, w2), w3)) & 0x7FFFFFFFu;
 }
 
+// Scale bytes written straight into the attention kernel's per-tile operand order (the
+// layout of mxattn_arrange_scales, 512 bytes per 128-key tile and head), for the forward's
+// own K^ and V^T.  K: the byte of key `key`, d-block b sits in dword 2 lane + b / 2, byte
+// t, of tile key / 128, with lane = r + 32 (b % 2) and (t, r) the inverse of the kernel's
+// key permutation kappa(t, r) = 64(t/2) + 32((r/4)%2) + 16(t%2) + 4(r/8) + r%4.
+__device__ __forceinline__ int64_t arranged_k_offset(int64_t key, int b) {
+  const int k = (int)(key & 127);
+  const int t = 2 * (k >> 6) + ((k >> 4) & 1);
+  const int r = 8 * ((k >> 2) & 3) + 4 * ((k >> 5) & 1) + (k & 3);
+  return 512 * (key >> 7) + 4 * (2 * (r + 32 * (b & 1)) + (b >> 1)) + t;
+}
+// V^T: the byte of channel ch, 32-key block kb sits in dword 2 lane + (kb / 2) % 2, byte
+// ch / 32, of tile kb / 4, with lane = ch % 32 + 32 (kb % 2).
+__device__ __forceinline__ int64_t arranged_v_offset(int ch, int64_t kb) {
+  return 512 * (kb >> 2) + 4 * (2 * ((ch & 31) + 32 * (int)(kb & 1)) + (int)((kb >> 1) & 1)) + (ch >> 5);
+}
+// (head, row within the head) of a global row, rows_per_head >= 1; 32-bit division when
+// every row index fits (the common case: B H N < 2^31), 64-bit otherwise.
+__device__ __forceinline__ void split_row(int64_t row, int64_t rows_per_head, int64_t nrows, int64_t& head,
+                                          int64_t& r) {
+  if (nrows < (int64_t(1) << 31)) {
+    const uint32_t h = (uint32_t)row / (uint32_t)rows_per_head;
+    head = h;
+    r = (uint32_t)row - h * (uint32_t)rows_per_head;
+  } else {
+    head = row / rows_per_head;
+    r = row - head * rows_per_head;
+  }
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Global->LDS DMA of 16, 4 or 2 bytes per lane through a raw buffer descriptor:

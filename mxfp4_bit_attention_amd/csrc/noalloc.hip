@@ -6,8 +6,11 @@
 // stand-in, so its device address is looked up once per device with
 // hipGetSymbolAddress, with that device current, and that address is what the kernels
 // receive.  Every call on one GPU uses that GPU's copy: calls that overlap in time on
-// one GPU race.  The pipeline rewrites every workspace byte it reads (K^, the padded
-// V^T, the re-ordered scales) before reading it, so nothing needs clearing between calls.
+// one GPU race.  Nothing needs clearing between calls: the pipeline rewrites every
+// workspace byte whose value reaches the output (K^, the padded V^T, their scales in the
+// attention kernel's operand order) before reading it; the only bytes it reads without
+// rewriting are the scales of the key slots past the last key, which feed logits the
+// kernel then masks, and at d = 64 the operand bytes that no MFMA selects.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>

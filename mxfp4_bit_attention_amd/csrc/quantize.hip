@@ -94,11 +94,14 @@ struct HadGeo {
   }
 };
 
-template <int D, int EB, bool ERR>
+// ARR: scales go straight into the attention kernel's operand order (arr_keys rows per
+// head, 4 arr_pad bytes per head) instead of [nrows, D/32].
+template <int D, int EB, bool ERR, bool ARR>
 __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restrict__ x, int64_t nrows,
                                                         uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales, Rule rule,
-                                                        float c, int64_t nchunks, double* err) {
+                                                        float c, int64_t nchunks, double* err, int64_t arr_keys,
+                                                        int64_t arr_pad) {
   using G = HadGeo<D, EB>;
   constexpr int LPR = G::LPR;
   __shared__ __attribute__((aligned(16))) uint8_t lds[G::NW * G::CB];
@@ -143,7 +146,15 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
       uint8_t* crow = codes + prow * (D / 2) + half * 32;
       *reinterpret_cast<uint4*>(crow) = make_uint4(q[0][0], q[0][1], q[0][2], q[0][3]);
       *reinterpret_cast<uint4*>(crow + 16) = make_uint4(q[1][0], q[1][1], q[1][2], q[1][3]);
-      *reinterpret_cast<uint16_t*>(scales + prow * (D / 32) + half * 2) = (uint16_t)sb2;
+      if constexpr (ARR) {
+        int64_t head, key;
+        split_row(prow, arr_keys, nrows, head, key);
+        uint8_t* hs = scales + head * (4 * arr_pad);
+        hs[arranged_k_offset(key, 2 * half)] = (uint8_t)sb2;
+        hs[arranged_k_offset(key, 2 * half + 1)] = (uint8_t)(sb2 >> 8);
+      } else {
+        *reinterpret_cast<uint16_t*>(scales + prow * (D / 32) + half * 2) = (uint16_t)sb2;
+      }
     }
   };
   if (chunk < nchunks) issue(chunk);
@@ -228,10 +239,13 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
 
 // ---------------------------------------------------------------------------
 // Plain quantise along the last axis: one thread per 32-element block.
-template <int EB, bool ERR>
+// ARR: scales in the attention kernel's operand order, blocks_per_row blocks per row and
+// arr_keys rows per head (4 arr_pad bytes per head).
+template <int EB, bool ERR, bool ARR>
 __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ x, int64_t nblocks,
                                                     uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, Rule rule, double* err) {
+                                                    uint8_t* __restrict__ scales, Rule rule, double* err,
+                                                    int blocks_per_row, int64_t arr_keys, int64_t arr_pad) {
   const int64_t blk0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (!ERR && blk0 >= nblocks) return;
   const bool valid = blk0 < nblocks;
@@ -272,7 +286,14 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
     acc.flush(err);
   } else {
     *reinterpret_cast<uint4*>(codes + blk * 16) = make_uint4(q[0], q[1], q[2], q[3]);
-    scales[blk] = sb;
+    if constexpr (ARR) {
+      const int64_t row = blk / blocks_per_row;
+      int64_t head, key;
+      split_row(row, arr_keys, nblocks / blocks_per_row, head, key);
+      scales[head * (4 * arr_pad) + arranged_k_offset(key, (int)(blk - row * blocks_per_row))] = sb;
+    } else {
+      scales[blk] = sb;
+    }
   }
 }
 
@@ -290,7 +311,9 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
 // tiles that complete each other's partial 128-byte lines of codes and scales (a
 // channel's row is not a multiple of 128 bytes) then write through the same L2.
 
-template <int EB, bool ERR>
+// ARR: scales in the attention kernel's operand order (one head per batch item, 4 P bytes
+// per head) instead of [batch, cols, P/32].
+template <int EB, bool ERR, bool ARR>
 __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ x, int64_t rows,
                                                     int64_t cols, int64_t P, int64_t batch,
                                                     uint8_t* __restrict__ codes,
@@ -370,7 +393,8 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
     if constexpr (!ERR) {
       const int64_t crow = b * cols + col + s;
       *reinterpret_cast<uint4*>(codes + crow * (P / 2) + kv0 / 2) = make_uint4(q[0], q[1], q[2], q[3]);
-      scales[crow * (P / 32) + kv0 / 32] = sb;
+      if constexpr (ARR) scales[b * (4 * P) + arranged_v_offset((int)(col + s), kv0 / 32)] = sb;
+      else scales[crow * (P / 32) + kv0 / 32] = sb;
     }
   }
   if constexpr (ERR) acc.flush(err);
@@ -386,13 +410,18 @@ __global__ void k_zero_f64(double* p, int n) {
 // store nothing and add the quantisation error sums to err[0..2] (the Qmax sweep).
 template <int D, int EB, bool ERR>
 static void launch_h(unsigned grid, const uint8_t* x, int64_t nrows, uint8_t* codes, uint8_t* scales, Rule rule,
-                     float c, int64_t nchunks, double* err, hipStream_t s) {
-  hipLaunchKernelGGL((k_quant_hadamard<D, EB, ERR>), dim3(grid), dim3(256), 0, s, x, nrows, codes, scales, rule, c,
-                     nchunks, err);
+                     float c, int64_t nchunks, double* err, int64_t arr_keys, int64_t arr_pad, hipStream_t s) {
+  if (!ERR && arr_keys > 0)
+    hipLaunchKernelGGL((k_quant_hadamard<D, EB, false, true>), dim3(grid), dim3(256), 0, s, x, nrows, codes, scales,
+                       rule, c, nchunks, err, arr_keys, arr_pad);
+  else
+    hipLaunchKernelGGL((k_quant_hadamard<D, EB, ERR, false>), dim3(grid), dim3(256), 0, s, x, nrows, codes, scales,
+                       rule, c, nchunks, err, arr_keys, arr_pad);
 }
 
 hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, uint8_t* codes,
-                                 uint8_t* scales, Rule rule, float c, double* err, hipStream_t s) {
+                                 uint8_t* scales, Rule rule, float c, double* err, hipStream_t s, int64_t arr_keys,
+                                 int64_t arr_pad) {
   const int rows_per_chunk = 64 / (d / 64);
   const int64_t nchunks = (nrows + rows_per_chunk - 1) / rows_per_chunk;
   // persistent waves: as many 4-wave workgroups as fit on the 256 CUs at once (three
@@ -403,14 +432,15 @@ hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, ui
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   const unsigned g = (unsigned)grid;
   const bool e = err != nullptr;
-  if (d == 128 && eb == 2) e ? launch_h<128, 2, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
-                             : launch_h<128, 2, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
-  else if (d == 128 && eb == 4) e ? launch_h<128, 4, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
-                                  : launch_h<128, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
-  else if (d == 64 && eb == 2) e ? launch_h<64, 2, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
-                                 : launch_h<64, 2, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
-  else if (d == 64 && eb == 4) e ? launch_h<64, 4, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s)
-                                 : launch_h<64, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, s);
+  const int64_t ak = arr_keys, ap = arr_pad;
+  if (d == 128 && eb == 2) e ? launch_h<128, 2, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s)
+                             : launch_h<128, 2, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s);
+  else if (d == 128 && eb == 4) e ? launch_h<128, 4, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s)
+                                  : launch_h<128, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s);
+  else if (d == 64 && eb == 2) e ? launch_h<64, 2, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s)
+                                 : launch_h<64, 2, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s);
+  else if (d == 64 && eb == 4) e ? launch_h<64, 4, true>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s)
+                                 : launch_h<64, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -422,35 +452,53 @@ hipError_t launch_zero_f64(double* p, int n, hipStream_t s) {
 }
 
 hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* codes, uint8_t* scales,
-                             Rule rule, double* err, hipStream_t s) {
+                             Rule rule, double* err, hipStream_t s, int blocks_per_row, int64_t arr_keys,
+                             int64_t arr_pad) {
   const int64_t grid = (nblocks + 255) / 256;
   const uint8_t* xp = static_cast<const uint8_t*>(x);
   const dim3 g((unsigned)grid), b(256);
-  if (eb == 2 && err) hipLaunchKernelGGL((k_quant_last<2, true>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
-  else if (eb == 2) hipLaunchKernelGGL((k_quant_last<2, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
-  else if (err) hipLaunchKernelGGL((k_quant_last<4, true>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
-  else hipLaunchKernelGGL((k_quant_last<4, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err);
+  const bool arr = !err && arr_keys > 0;
+  if (arr && (blocks_per_row < 1 || nblocks % blocks_per_row)) return hipErrorInvalidValue;
+  const int bpr = blocks_per_row;
+  if (eb == 2 && err)
+    hipLaunchKernelGGL((k_quant_last<2, true, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err, bpr,
+                       arr_keys, arr_pad);
+  else if (eb == 2 && arr)
+    hipLaunchKernelGGL((k_quant_last<2, false, true>), g, b, 0, s, xp, nblocks, codes, scales, rule, err, bpr,
+                       arr_keys, arr_pad);
+  else if (eb == 2)
+    hipLaunchKernelGGL((k_quant_last<2, false, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err, bpr,
+                       arr_keys, arr_pad);
+  else if (err)
+    hipLaunchKernelGGL((k_quant_last<4, true, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err, bpr,
+                       arr_keys, arr_pad);
+  else if (arr)
+    hipLaunchKernelGGL((k_quant_last<4, false, true>), g, b, 0, s, xp, nblocks, codes, scales, rule, err, bpr,
+                       arr_keys, arr_pad);
+  else
+    hipLaunchKernelGGL((k_quant_last<4, false, false>), g, b, 0, s, xp, nblocks, codes, scales, rule, err, bpr,
+                       arr_keys, arr_pad);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
-                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s) {
+                             int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s,
+                             bool arranged) {
   const int64_t tiles = (P + 255) / 256 * ((cols + 63) / 64) * batch;
   if (tiles > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tiles + 7) / 8 * 8));
   const uint8_t* xp = static_cast<const uint8_t*>(x);
-  if (eb == 2 && err)
-    hipLaunchKernelGGL((k_quant_rows<2, true>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
-                       err);
-  else if (eb == 2)
-    hipLaunchKernelGGL((k_quant_rows<2, false>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
-                       err);
-  else if (err)
-    hipLaunchKernelGGL((k_quant_rows<4, true>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
-                       err);
-  else
-    hipLaunchKernelGGL((k_quant_rows<4, false>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, rule,
-                       err);
+  const bool arr = arranged && !err;
+#define MX_ROWS(EB_, ERR_, ARR_)                                                                                 \
+  hipLaunchKernelGGL((k_quant_rows<EB_, ERR_, ARR_>), grid, dim3(256), 0, s, xp, rows, cols, P, batch, codes, scales, \
+                     rule, err)
+  if (eb == 2 && err) MX_ROWS(2, true, false);
+  else if (eb == 2 && arr) MX_ROWS(2, false, true);
+  else if (eb == 2) MX_ROWS(2, false, false);
+  else if (err) MX_ROWS(4, true, false);
+  else if (arr) MX_ROWS(4, false, true);
+  else MX_ROWS(4, false, false);
+#undef MX_ROWS
   return hipGetLastError();
 }
 
