@@ -152,7 +152,7 @@ def tile_mix_ceiling(den: dict, d: int, achieved: float) -> dict:
     """The attention tile's own instruction mix timed alone (no memory, LDS or barrier;
     three waves per SIMD as the kernel runs): the TFLOP/s the kernel would reach if every
     32-query x 128-key wave-tile cost only that, at the clock that mix sustains."""
-    m = den["attention_tile_mix"]
+    m = den["attention_tile_mix" if d == 128 else "attention_tile_mix_d64"]
     simds = 4 * den["compute_units"]
     peak = 4.0 * 32 * 128 * d * simds * m["clock_MHz"] * 1e6 / m["cycles_per_trip_per_wave"] / 1e12
     return {"cycles_per_wave_tile": m["cycles_per_trip_per_wave"], "clock_MHz": m["clock_MHz"],
@@ -423,6 +423,9 @@ def main():
 
     if not args.no_extras:
         result.update(extras(torch, mx, w, q, k, v, out, ws, stream))
+        if "denominators" in result:
+            d64 = result["other_shapes"]["d64"]
+            d64["tile_mix"] = tile_mix_ceiling(result["denominators"], 64, d64["TFLOPs"])
     del q, k, v, out, ws
 
     if not args.no_cpu_baseline:

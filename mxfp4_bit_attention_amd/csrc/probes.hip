@@ -95,10 +95,12 @@ __global__ __launch_bounds__(256) void k_valu(int64_t iters, float seed, unsigne
 }
 
 // The attention kernel's per-tile instruction mix with no memory, LDS or barrier: per
-// trip and wave, 18 fp4 32x32x64 MFMAs (four accumulator chains), 65 v_exp_f32, 32 fp4
-// conversions, 65 fp32 FMAs and 34 NaN-propagating max3, the counts of one 32-query x
-// 128-key tile of the attention's inner loop (d = 128).  With three waves per SIMD, as
-// the attention kernel runs, its time per trip is the cost of that mix on its own.
+// trip and wave, NMFMA fp4 32x32x64 MFMAs (four accumulator chains; 18 at d = 128, 10 at
+// d = 64), 65 v_exp_f32, 32 fp4 conversions, 65 fp32 FMAs and 34 NaN-propagating max3,
+// the counts of one 32-query x 128-key tile of the attention's inner loop.  With three
+// waves per SIMD, as the attention kernel runs, its time per trip is the cost of that mix
+// on its own.
+template <int NMFMA>
 __global__ __launch_bounds__(256, 3) void k_mix(int64_t iters, int code, unsigned long long* st) {
   const v8i a = {code, code, code, code, 0, 0, 0, 0};
   const v8i b = {code ^ (int)threadIdx.x, code, code, code, 0, 0, 0, 0};
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256, 3) void k_mix(int64_t iters, int code, unsigne
   const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
   for (int64_t i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int k = 0; k < 18; ++k) c[k & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[k & 3], 4, 4, 0, 127, 0, 127);
+    for (int k = 0; k < NMFMA; ++k) c[k & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[k & 3], 4, 4, 0, 127, 0, 127);
     // the max3 operands change every step, so no two of them can be folded
 #pragma unroll
     for (int k = 0; k < 65; ++k) {
@@ -266,12 +268,16 @@ int32_t mxprobe_valu(int32_t kind, int64_t iters, int32_t waves_per_simd, uint64
   return status(hipGetLastError());
 }
 
-// The attention tile's instruction mix (k_mix), three waves per SIMD.
-int32_t mxprobe_mix(int64_t iters, uint64_t* stats, void* stream) {
+// The attention tile's instruction mix (k_mix) for head dimension d (128 or 64), three
+// waves per SIMD.
+int32_t mxprobe_mix(int64_t iters, int32_t d, uint64_t* stats, void* stream) {
   const int cus = cu_count();
-  if (iters < 1 || !stats || cus < 1) return -1;
-  hipLaunchKernelGGL(k_mix, dim3(cus * 3), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 0x22222222,
-                     reinterpret_cast<unsigned long long*>(stats));
+  if (iters < 1 || !stats || cus < 1 || (d != 128 && d != 64)) return -1;
+  unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
+  if (d == 128)
+    hipLaunchKernelGGL(k_mix<18>, dim3(cus * 3), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 0x22222222, st);
+  else
+    hipLaunchKernelGGL(k_mix<10>, dim3(cus * 3), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 0x22222222, st);
   return status(hipGetLastError());
 }
 

@@ -225,14 +225,23 @@ def test_full_size_d64_sampled_rows():
     _full_size_case(w)
 
 
-def test_repeatable_bitwise():
+@pytest.mark.parametrize("d", [128, 64])
+def test_repeatable_bitwise(d):
+    """The forward ten times, and the quantised entry with its P^ dump ten times, on the
+    same inputs: bitwise identical outputs and dumps (a race on the three-stage LDS ring,
+    its DMAs or the barrier would show as a run-to-run difference)."""
     torch, mx = require_gpu()
     g = torch.Generator(device="cuda").manual_seed(1)
-    q, k, v = (torch.randn((1, 3, 3000, 128), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
-    outs = [mx.mxattn_forward(q, k, v, 0.0883883, hadamard=True, pnq=True, rule="uos") for _ in range(3)]
+    q, k, v = (torch.randn((1, 3, 3000, d), generator=g, device="cuda").to(torch.bfloat16) for _ in range(3))
+    outs = [mx.mxattn_forward(q, k, v, d ** -0.5, hadamard=True, pnq=True, rule="uos") for _ in range(10)]
     torch.cuda.synchronize()
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+    ops = _device_operands(1, 2, 700, 1500, d, seed=d)
+    dumps = [mx.mxattn_forward_quantized(*ops, 1500, d ** -0.5, pnq=True, p_rule="uos", dump_p=True) for _ in range(10)]
+    torch.cuda.synchronize()
+    for o, pc, ps in dumps[1:]:
+        assert torch.equal(o, dumps[0][0]) and torch.equal(pc, dumps[0][1]) and torch.equal(ps, dumps[0][2])
 
 
 @pytest.mark.parametrize("dtype,d,had,rule", [("bf16", 128, True, "uos"), ("bf16", 128, False, "ocp"),

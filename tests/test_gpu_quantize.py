@@ -174,10 +174,14 @@ def test_full_size_quantize_pass_every_head():
         assert not bad, f"{rule}: heads {bad} differ from the oracle's digests"
 
 
-def test_repeatable_bitwise():
+@pytest.mark.parametrize("axis,had", [("last", True), ("last", False), ("rows", False)])
+def test_repeatable_bitwise(axis, had):
+    """Each quantiser ten times on the same input: bitwise identical codes and scales (a
+    race on the LDS staging buffers would show as a run-to-run difference)."""
     torch, mx = require_gpu()
-    x = torch.randn((8, 3000, 128), device="cuda").to(torch.bfloat16)
-    outs = [mx.mxattn_quantize(x, rule="uos", axis="last", hadamard=True) for _ in range(3)]
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn((8, 3000, 128), generator=g, device="cuda").to(torch.bfloat16)
+    outs = [mx.mxattn_quantize(x, rule="uos", axis=axis, hadamard=had) for _ in range(10)]
     torch.cuda.synchronize()
     for c, s in outs[1:]:
         assert torch.equal(c, outs[0][0]) and torch.equal(s, outs[0][1])
