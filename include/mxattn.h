@@ -153,7 +153,10 @@ size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t 
  *   1. Q and K: optional Hadamard rotation along d, then block quantisation along d
  *      (K by the quantiser into the workspace; Q by the attention kernel as it loads
  *      its query rows -- the same arithmetic, so the same codes as mxattn_quantize).
- *   2. V: block quantisation along tokens.
+ *   2. V: block quantisation along tokens.  The scales of K^ and V^T go into the
+ *      workspace directly in the order of mxattn_arrange_scales (the same bytes that
+ *      mxattn_quantize followed by mxattn_arrange_scales would give, apart from the
+ *      slots of keys past Nkv, which are left unwritten and whose logits are masked).
  *   3. FlashAttention-2 online softmax over kv tiles of mxattn_kv_tile() keys, in
  *      increasing order.  Per tile: S = scale * (Q^ K^^T) on block-scaled MFMA;
  *      m' = max(m, rowmax S); alpha = exp(m - m'); P~ = exp(S - m').
