@@ -155,8 +155,12 @@ def tile_mix_ceiling(den: dict, d: int, achieved: float) -> dict:
     m = den["attention_tile_mix" if d == 128 else "attention_tile_mix_d64"]
     simds = 4 * den["compute_units"]
     peak = 4.0 * 32 * 128 * d * simds * m["clock_MHz"] * 1e6 / m["cycles_per_trip_per_wave"] / 1e12
-    return {"cycles_per_wave_tile": m["cycles_per_trip_per_wave"], "clock_MHz": m["clock_MHz"],
-            "peak_TFLOPs": round(peak, 1), "frac": round(achieved / peak, 4)}
+    out = {"cycles_per_wave_tile": m["cycles_per_trip_per_wave"], "clock_MHz": m["clock_MHz"],
+           "peak_TFLOPs": round(peak, 1), "frac": round(achieved / peak, 4)}
+    for k in ("valu_only_cycles", "mfma_only_cycles", "mfma_hidden"):
+        if k in m:
+            out[k] = m[k]
+    return out
 
 
 def _blas_threads() -> int:

@@ -99,8 +99,10 @@ __global__ __launch_bounds__(256) void k_valu(int64_t iters, float seed, unsigne
 // d = 64), 65 v_exp_f32, 32 fp4 conversions, 65 fp32 FMAs and 34 NaN-propagating max3,
 // the counts of one 32-query x 128-key tile of the attention's inner loop.  With three
 // waves per SIMD, as the attention kernel runs, its time per trip is the cost of that mix
-// on its own.
-template <int NMFMA>
+// on its own.  VALU = false keeps only the MFMAs, NMFMA = 0 only the vector instructions:
+// the two parts alone against the whole show how much of the MFMA time the vector work
+// hides.
+template <int NMFMA, bool VALU = true>
 __global__ __launch_bounds__(256, 3) void k_mix(int64_t iters, int code, unsigned long long* st) {
   const v8i a = {code, code, code, code, 0, 0, 0, 0};
   const v8i b = {code ^ (int)threadIdx.x, code, code, code, 0, 0, 0, 0};
@@ -120,20 +122,22 @@ __global__ __launch_bounds__(256, 3) void k_mix(int64_t iters, int code, unsigne
   for (int64_t i = 0; i < iters; ++i) {
 #pragma unroll
     for (int k = 0; k < NMFMA; ++k) c[k & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[k & 3], 4, 4, 0, 127, 0, 127);
-    // the max3 operands change every step, so no two of them can be folded
+    if constexpr (VALU) {
+      // the max3 operands change every step, so no two of them can be folded
 #pragma unroll
-    for (int k = 0; k < 65; ++k) {
-      x[k & 7] = __builtin_amdgcn_exp2f(-x[k & 7]);
-      y[k & 7] = __builtin_fmaf(y[k & 7], fa, fb);
-      if (k < 34)
-        z[k & 7] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(z[k & 7], x[k & 7]), y[k & 7]);
-    }
+      for (int k = 0; k < 65; ++k) {
+        x[k & 7] = __builtin_amdgcn_exp2f(-x[k & 7]);
+        y[k & 7] = __builtin_fmaf(y[k & 7], fa, fb);
+        if (k < 34)
+          z[k & 7] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(z[k & 7], x[k & 7]), y[k & 7]);
+      }
 #pragma unroll
-    for (int k = 0; k < 32; k += 4) {
-      r[k & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[k & 7], x[k & 7], y[k & 7], 1.0f, 0);
-      r[k & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[k & 7], x[(k + 1) & 7], y[(k + 1) & 7], 1.0f, 1);
-      r[(k + 1) & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[(k + 1) & 7], x[(k + 2) & 7], y[(k + 2) & 7], 1.0f, 2);
-      r[(k + 1) & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[(k + 1) & 7], x[(k + 3) & 7], y[(k + 3) & 7], 1.0f, 3);
+      for (int k = 0; k < 32; k += 4) {
+        r[k & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[k & 7], x[k & 7], y[k & 7], 1.0f, 0);
+        r[k & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[k & 7], x[(k + 1) & 7], y[(k + 1) & 7], 1.0f, 1);
+        r[(k + 1) & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[(k + 1) & 7], x[(k + 2) & 7], y[(k + 2) & 7], 1.0f, 2);
+        r[(k + 1) & 7] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r[(k + 1) & 7], x[(k + 3) & 7], y[(k + 3) & 7], 1.0f, 3);
+      }
     }
   }
   float keep = 0.0f;
@@ -269,15 +273,18 @@ int32_t mxprobe_valu(int32_t kind, int64_t iters, int32_t waves_per_simd, uint64
 }
 
 // The attention tile's instruction mix (k_mix) for head dimension d (128 or 64), three
-// waves per SIMD.
-int32_t mxprobe_mix(int64_t iters, int32_t d, uint64_t* stats, void* stream) {
+// waves per SIMD.  part: 0 the whole mix, 1 its vector instructions only, 2 its MFMAs only.
+int32_t mxprobe_mix(int64_t iters, int32_t d, int32_t part, uint64_t* stats, void* stream) {
   const int cus = cu_count();
-  if (iters < 1 || !stats || cus < 1 || (d != 128 && d != 64)) return -1;
+  if (iters < 1 || !stats || cus < 1 || (d != 128 && d != 64) || part < 0 || part > 2) return -1;
   unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
-  if (d == 128)
-    hipLaunchKernelGGL(k_mix<18>, dim3(cus * 3), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 0x22222222, st);
-  else
-    hipLaunchKernelGGL(k_mix<10>, dim3(cus * 3), dim3(256), 0, static_cast<hipStream_t>(stream), iters, 0x22222222, st);
+  const dim3 g(cus * 3), b(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (part == 1) hipLaunchKernelGGL((k_mix<0, true>), g, b, 0, s, iters, 0x22222222, st);
+  else if (d == 128 && part == 0) hipLaunchKernelGGL((k_mix<18, true>), g, b, 0, s, iters, 0x22222222, st);
+  else if (d == 128) hipLaunchKernelGGL((k_mix<18, false>), g, b, 0, s, iters, 0x22222222, st);
+  else if (part == 0) hipLaunchKernelGGL((k_mix<10, true>), g, b, 0, s, iters, 0x22222222, st);
+  else hipLaunchKernelGGL((k_mix<10, false>), g, b, 0, s, iters, 0x22222222, st);
   return status(hipGetLastError());
 }
 

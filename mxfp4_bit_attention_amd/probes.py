@@ -42,7 +42,7 @@ def _load():
     lib.mxprobe_hbm_copy.restype = i32
     lib.mxprobe_hbm_copy.argtypes = [vp, vp, u64, i32, i32, vp]
     lib.mxprobe_mix.restype = i32
-    lib.mxprobe_mix.argtypes = [i64, i32, vp, vp]
+    lib.mxprobe_mix.argtypes = [i64, i32, i32, vp, vp]
     lib.mxprobe_hbm_dma.restype = i32
     lib.mxprobe_hbm_dma.argtypes = [vp, vp, u64, i32, i32, vp, vp]
     return lib
@@ -120,15 +120,28 @@ def measure(torch, device=None, hbm_bytes: int = 1 << 31) -> dict:
     out["exp_fma_interleaved"] = {"cycles_per_instruction_3w": round(mix, 2), "apart_mean": round(apart, 2),
                                   "overlap": "none" if mix >= 0.97 * apart else "partial"}
 
-    # --- the attention tile's instruction mix alone (three waves per SIMD), d = 128 and 64
+    # --- the attention tile's instruction mix alone (three waves per SIMD), d = 128 and 64,
+    # and its two parts on their own: the vector instructions only, the MFMAs only
     it = 2000
+
+    def mix(d, part):
+        ms, clk = _run(torch, lambda st: lib.mxprobe_mix(it, d, part, st, sp), stream, dev, wall_khz)
+        return ms, clk, ms * 1e-3 * clk * 1e6 / (3 * it)
+
     for d, key in ((128, "attention_tile_mix"), (64, "attention_tile_mix_d64")):
-        ms, clk = _run(torch, lambda st: lib.mxprobe_mix(it, d, st, sp), stream, dev, wall_khz)
+        ms, clk, cyc = mix(d, 0)
         out[key] = {
             "per_trip": {"mfma_32x32x64": 18 if d == 128 else 10, "v_exp_f32": 65, "fp4_cvt": 32, "v_fma_f32": 65,
                          "v_maximum3_f32": 34},
-            "cycles_per_trip_per_wave": round(ms * 1e-3 * clk * 1e6 / (3 * it), 1),
+            "cycles_per_trip_per_wave": round(cyc, 1),
             "clock_MHz": round(clk, 1), "ms": round(ms, 3)}
+    _, _, valu_only = mix(128, 1)
+    _, _, mfma_only = mix(128, 2)
+    whole = out["attention_tile_mix"]["cycles_per_trip_per_wave"]
+    out["attention_tile_mix"]["valu_only_cycles"] = round(valu_only, 1)
+    out["attention_tile_mix"]["mfma_only_cycles"] = round(mfma_only, 1)
+    # share of the MFMA time that runs under the vector work
+    out["attention_tile_mix"]["mfma_hidden"] = round((valu_only + mfma_only - whole) / mfma_only, 3)
 
     # --- HBM streaming, best of a few launch shapes
     n = hbm_bytes
