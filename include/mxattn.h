@@ -157,6 +157,8 @@ size_t mxattn_forward_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t 
  *      workspace directly in the order of mxattn_arrange_scales (the same bytes that
  *      mxattn_quantize followed by mxattn_arrange_scales would give, apart from the
  *      slots of keys past Nkv, which are left unwritten and whose logits are masked).
+ *      With the rotation and K, V of at most 128 MiB each, K's and V's quantisation
+ *      run as one kernel launch, otherwise as two; the bytes written are the same.
  *   3. FlashAttention-2 online softmax over kv tiles of mxattn_kv_tile() keys, in
  *      increasing order.  Per tile: S = scale * (Q^ K^^T) on block-scaled MFMA;
  *      m' = max(m, rowmax S); alpha = exp(m - m'); P~ = exp(S - m').

@@ -46,6 +46,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;
 // Tokens per head (Nq, Nkv) of the attention entry points: keeps every per-head byte
 // count of the kernels below 2^31.
 constexpr int64_t kMaxTokens = int64_t(1) << 24;
+// Largest K (and V) input, in bytes, that the forward quantises in one joint launch.
+constexpr int64_t kJointQuantBytes = int64_t(128) << 20;
 
 bool mul_ok(int64_t a, int64_t b, int64_t limit, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -379,12 +381,21 @@ int mxattn_forward(const void* Q, const void* K, const void* V, int32_t dtype, i
   const int64_t P = round_up(Nkv, mxattn::kKvTile);
   const float c = inv_sqrt_f32((int)d);
   hipError_t e;
-  // K^ and V^T with their scales already in the attention kernel's operand order
-  if (hadamard)
-    e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ksa, rule, c, nullptr, s, Nkv, P);
-  else
-    e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ksa, rule, nullptr, s, (int)(d / 32), Nkv, P);
-  if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vsa, rule, nullptr, s, true);
+  // K^ and V^T with their scales already in the attention kernel's operand order.  For a
+  // small K and V (a few thousand tokens) both go in one launch, which saves a launch's
+  // ramp (6 us of a 74 us step at 40 heads x 2048 tokens); for larger ones two launches
+  // are faster, since in the joint kernel the token-axis quantiser runs at the Hadamard
+  // quantiser's register count, three workgroups per CU instead of five.
+  const bool joint = hadamard && B * H * Nkv * d * eb <= kJointQuantBytes;
+  if (joint) {
+    e = mxattn::launch_quant_kv(K, V, eb, (int)d, B * H, Nkv, P, kc, ksa, vc, vsa, rule, c, s);
+  } else {
+    if (hadamard)
+      e = mxattn::launch_quant_hadamard(K, eb, (int)d, B * H * Nkv, kc, ksa, rule, c, nullptr, s, Nkv, P);
+    else
+      e = mxattn::launch_quant_last(K, eb, B * H * Nkv * d / 32, kc, ksa, rule, nullptr, s, (int)(d / 32), Nkv, P);
+    if (e == hipSuccess) e = mxattn::launch_quant_rows(V, eb, B * H, Nkv, d, P, vc, vsa, rule, nullptr, s, true);
+  }
   if (e != hipSuccess) return hip_fail(e, who);
   // Q is read once per query tile: the attention kernel rotates and quantises it itself
   const QuantQ fused{Q, eb == 2, hadamard != 0, c};

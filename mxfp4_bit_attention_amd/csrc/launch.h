@@ -36,6 +36,10 @@ hipError_t launch_quant_last(const void* x, int eb, int64_t nblocks, uint8_t* co
 hipError_t launch_quant_rows(const void* x, int eb, int64_t batch, int64_t rows, int64_t cols,
                              int64_t P, uint8_t* codes, uint8_t* scales, Rule rule, double* err, hipStream_t s,
                              bool arranged = false);
+// The forward's K and V in one launch: the Hadamard quantiser over K [heads, nkv, d] and the
+// token-axis quantiser over V [heads, nkv, d], both with arranged scales (P padded tokens).
+hipError_t launch_quant_kv(const void* k, const void* v, int eb, int d, int64_t heads, int64_t nkv, int64_t P,
+                          uint8_t* kc, uint8_t* ksa, uint8_t* vc, uint8_t* vsa, Rule rule, float c, hipStream_t s);
 // Sets n doubles to zero with a kernel (graph-capturable, unlike a memset node).
 hipError_t launch_zero_f64(double* p, int n, hipStream_t s);
 

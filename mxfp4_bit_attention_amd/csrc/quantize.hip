@@ -96,20 +96,21 @@ struct HadGeo {
 
 // ARR: scales go straight into the attention kernel's operand order (arr_keys rows per
 // head, 4 arr_pad bytes per head) instead of [nrows, D/32].
+// The body runs as workgroup `bid` of `nblk` with `lds` (NW * CB bytes) as its buffers,
+// so that the forward can launch it together with the token-axis quantiser.
 template <int D, int EB, bool ERR, bool ARR>
-__global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restrict__ x, int64_t nrows,
-                                                        uint8_t* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, Rule rule,
-                                                        float c, int64_t nchunks, double* err, int64_t arr_keys,
-                                                        int64_t arr_pad) {
+__device__ __forceinline__ void quant_hadamard_body(uint8_t* lds, int bid, int nblk, const uint8_t* __restrict__ x,
+                                                    int64_t nrows, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales, Rule rule, float c,
+                                                    int64_t nchunks, double* err, int64_t arr_keys,
+                                                    int64_t arr_pad) {
   using G = HadGeo<D, EB>;
   constexpr int LPR = G::LPR;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[G::NW * G::CB];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint8_t* buf = lds + wave * G::CB;
-  const int64_t W = (int64_t)gridDim.x * G::NW;
-  int64_t chunk = (int64_t)blockIdx.x * G::NW + wave;
+  const int64_t W = (int64_t)nblk * G::NW;
+  int64_t chunk = (int64_t)bid * G::NW + wave;
   const int64_t total = nrows * G::RB;
 
   // per-lane DMA source offsets within a chunk (the same for every chunk)
@@ -135,8 +136,8 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
   const int lr = lane / LPR;    // row within the chunk
   const int half = lane % LPR;  // which 64 elements of the row
   // The stores of a chunk are issued one iteration late, after the next chunk has
-  // been read from LDS: the wait the compiler places before those reads (for the DMA
-  // that filled the buffer) then never waits on stores issued just before it.
+  // been read from LDS: the wait for the DMA that filled the buffer, before those reads,
+  // then never waits on stores issued just before it.
   uint32_t q[2][4];
   uint32_t sb2 = 0;
   int64_t prow = -1;  // row whose results q / sb2 hold (-1: none)
@@ -159,6 +160,9 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
   };
   if (chunk < nchunks) issue(chunk);
   for (; chunk < nchunks; chunk += W) {
+    // wait until this chunk's DMA (the wave's newest vector-memory operation) has landed
+    // in LDS before reading it; the stores issued before it went out an iteration ago
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     float v[64];
     {
       const uint8_t* p = buf + lr * G::RB;
@@ -237,6 +241,18 @@ __global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restric
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) before the wave's LDS is released
 }
 
+template <int D, int EB, bool ERR, bool ARR>
+__global__ __launch_bounds__(256) void k_quant_hadamard(const uint8_t* __restrict__ x, int64_t nrows,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales, Rule rule,
+                                                        float c, int64_t nchunks, double* err, int64_t arr_keys,
+                                                        int64_t arr_pad) {
+  using G = HadGeo<D, EB>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::NW * G::CB];
+  quant_hadamard_body<D, EB, ERR, ARR>(lds, (int)blockIdx.x, (int)gridDim.x, x, nrows, codes, scales, rule, c,
+                                       nchunks, err, arr_keys, arr_pad);
+}
+
 // ---------------------------------------------------------------------------
 // Plain quantise along the last axis: one thread per 32-element block.
 // ARR: scales in the attention kernel's operand order, blocks_per_row blocks per row and
@@ -313,23 +329,31 @@ __global__ __launch_bounds__(256) void k_quant_last(const uint8_t* __restrict__ 
 
 // ARR: scales in the attention kernel's operand order (one head per batch item, 4 P bytes
 // per head) instead of [batch, cols, P/32].
+// The body runs as workgroup `bid` of `nblk` (a multiple of 8, with bid on the XCD that
+// hardware block bid would be dealt to) with `tile` (RowsGeo<EB>::LDS bytes) as its LDS.
+template <int EB>
+struct RowsGeo {
+  static constexpr int TT = 256;                   // tokens per tile
+  static constexpr int TC = 64;                    // columns per tile
+  static constexpr int RB = TC * EB;               // bytes of one tile row: 128 (bf16) or 256 (fp32)
+  static constexpr int CH = RB / 16;               // 16-byte units per tile row
+  static constexpr int NDMA = TT * RB / 1024 / 4;  // 1 KB DMAs per wave
+  static constexpr int LDS = TT * RB;
+};
+
 template <int EB, bool ERR, bool ARR>
-__global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t P, int64_t batch,
-                                                    uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales, Rule rule, double* err) {
-  constexpr int TT = 256;         // tokens per tile
-  constexpr int TC = 64;          // columns per tile
-  constexpr int RB = TC * EB;     // bytes of one tile row: 128 (bf16) or 256 (fp32)
-  constexpr int CH = RB / 16;     // 16-byte units per tile row
-  constexpr int NDMA = TT * RB / 1024 / 4;  // 1 KB DMAs per wave
-  __shared__ __attribute__((aligned(16))) uint8_t tile[TT * RB];
+__device__ __forceinline__ void quant_rows_body(uint8_t* tile, int bid, int nblk, const uint8_t* __restrict__ x,
+                                                int64_t rows, int64_t cols, int64_t P, int64_t batch,
+                                                uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, Rule rule,
+                                                double* err) {
+  using RG = RowsGeo<EB>;
+  constexpr int TT = RG::TT, TC = RG::TC, RB = RG::RB, CH = RG::CH, NDMA = RG::NDMA;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t nx = (P + TT - 1) / TT, ny = (cols + TC - 1) / TC;
-  const int64_t per_xcd = (int64_t)(gridDim.x / 8);
-  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int64_t per_xcd = (int64_t)(nblk / 8);
+  const int64_t item = (int64_t)(bid % 8) * per_xcd + bid / 8;
   if (item >= nx * ny * batch) return;
   const int64_t t0 = (item % nx) * TT;
   const int64_t c0 = ((item / nx) % ny) * TC;
@@ -400,6 +424,38 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ 
   if constexpr (ERR) acc.flush(err);
 }
 
+template <int EB, bool ERR, bool ARR>
+__global__ __launch_bounds__(256) void k_quant_rows(const uint8_t* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t P, int64_t batch,
+                                                    uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales, Rule rule, double* err) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[RowsGeo<EB>::LDS];
+  quant_rows_body<EB, ERR, ARR>(tile, (int)blockIdx.x, (int)gridDim.x, x, rows, cols, P, batch, codes, scales, rule,
+                                err);
+}
+
+// The forward's K and V quantisation in one launch: workgroups [0, nk) run the Hadamard
+// quantiser over K (scales in the attention kernel's operand order), the rest the
+// token-axis quantiser over V.  nk is a multiple of 8, so the V workgroups keep the
+// XCD dealing their numbering assumes.  The two bodies use LDS buffers of one size.
+template <int D, int EB>
+__global__ __launch_bounds__(256) void k_quant_kv(const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+                                                  int64_t heads, int64_t nkv, int64_t P, uint8_t* __restrict__ kc,
+                                                  uint8_t* __restrict__ ksa, uint8_t* __restrict__ vc,
+                                                  uint8_t* __restrict__ vsa, Rule rule, float c, int64_t nchunks,
+                                                  int nk) {
+  using G = HadGeo<D, EB>;
+  static_assert(G::NW * G::CB == RowsGeo<EB>::LDS, "one LDS size for both quantisers");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[G::NW * G::CB];
+  const int bid = (int)blockIdx.x;
+  if (bid < nk)
+    quant_hadamard_body<D, EB, false, true>(lds, bid, nk, k, heads * nkv, kc, ksa, rule, c, nchunks, nullptr, nkv,
+                                            P);
+  else
+    quant_rows_body<EB, false, true>(lds, bid - nk, (int)gridDim.x - nk, v, nkv, D, P, heads, vc, vsa, rule,
+                                     nullptr);
+}
+
 __global__ void k_zero_f64(double* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0;
@@ -443,6 +499,32 @@ hipError_t launch_quant_hadamard(const void* x, int eb, int d, int64_t nrows, ui
                                  : launch_h<64, 4, false>(g, xp, nrows, codes, scales, rule, c, nchunks, err, ak, ap, s);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_kv(const void* k, const void* v, int eb, int d, int64_t heads, int64_t nkv, int64_t P,
+                          uint8_t* kc, uint8_t* ksa, uint8_t* vc, uint8_t* vsa, Rule rule, float c, hipStream_t s) {
+  const int rows_per_chunk = 64 / (d / 64);
+  const int64_t nchunks = (heads * nkv + rows_per_chunk - 1) / rows_per_chunk;
+  int64_t nk = (nchunks + 3) / 4;  // persistent K workgroups, as launch_quant_hadamard sizes them
+  const int64_t resident = 256 * (eb == 2 ? 3 : 2);
+  if (nk > resident) nk = resident;
+  nk = (nk + 7) / 8 * 8;  // the extra workgroups find no chunk and return
+  const int64_t tiles = (P + 255) / 256 * ((d + 63) / 64) * heads;
+  const int64_t nv = (tiles + 7) / 8 * 8;
+  if (nk + nv > (int64_t)0x7FFFFFF0) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(nk + nv)), block(256);
+  const uint8_t* kp = static_cast<const uint8_t*>(k);
+  const uint8_t* vp = static_cast<const uint8_t*>(v);
+#define MX_KV(D_, EB_) \
+  hipLaunchKernelGGL((k_quant_kv<D_, EB_>), grid, block, 0, s, kp, vp, heads, nkv, P, kc, ksa, vc, vsa, rule, c, \
+                     nchunks, (int)nk)
+  if (d == 128 && eb == 2) MX_KV(128, 2);
+  else if (d == 128 && eb == 4) MX_KV(128, 4);
+  else if (d == 64 && eb == 2) MX_KV(64, 2);
+  else if (d == 64 && eb == 4) MX_KV(64, 4);
+  else return hipErrorInvalidValue;
+#undef MX_KV
   return hipGetLastError();
 }
 

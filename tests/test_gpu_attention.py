@@ -278,6 +278,28 @@ def test_fused_q_quantisation_is_bitwise_the_quantiser(dtype, d, had, rule):
     assert torch.equal(O.view(iv), O2.view(iv))
 
 
+@pytest.mark.parametrize("d,Nkv", [(128, 617), (128, 200_000), (64, 617), (64, 400_000)])
+def test_forward_joint_and_separate_kv_quantisation(d, Nkv):
+    """The forward quantises a small K and V (up to 128 MiB each) in one joint launch and a
+    larger one in two launches (200,000 and 400,000 keys x 3 heads in bf16 are above that
+    size at d = 128 and 64): either way its output is bitwise that of mxattn_quantize on
+    Q, K and V followed by mxattn_forward_quantized."""
+    torch, mx = require_gpu()
+    B, H, Nq = 1, 3, 300
+    g = torch.Generator(device="cuda").manual_seed(d + Nkv)
+    q, k, v = (torch.randn((B, H, n, d), generator=g, device="cuda").to(torch.bfloat16) for n in (Nq, Nkv, Nkv))
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    O = mx.mxattn_forward(q, k, v, scale, hadamard=True, pnq=True, rule="uos")
+    qc, qs = mx.mxattn_quantize(q.view(-1, Nq, d), rule="uos", axis="last", hadamard=True)
+    kc, ks = mx.mxattn_quantize(k.view(-1, Nkv, d), rule="uos", axis="last", hadamard=True)
+    vc, vs = mx.mxattn_quantize(v.view(-1, Nkv, d), rule="uos", axis="rows")
+    sh = lambda t: t.view(B, H, *t.shape[1:])
+    O2 = mx.mxattn_forward_quantized(sh(qc), sh(qs), sh(kc), sh(ks), sh(vc), sh(vs), Nkv, scale, pnq=True,
+                                     p_rule="uos", out_dtype=O.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O2.view(torch.int16))
+
+
 def _arranged_reference(ks, vts, Nkv, d):
     """The order mxattn_arrange_scales documents, written out on the host: per head and
     kv tile j, dword 2 lane + s byte t of K = key 128 j + kappa(t, lane % 32), block
