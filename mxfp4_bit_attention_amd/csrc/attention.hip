@@ -25,8 +25,9 @@
 // its duration (the 16x16x128 form does not), so ALU work placed beside these
 // MFMAs, in this wave or in the other waves of the SIMD, runs in their shadow.
 // The MFMAs' E8M0 scale operands come either pre-arranged per tile in the lanes'
-// operand order (k_arrange_scales; one 8-byte LDS read per lane and tile) or in the
-// quantiser's layout, from which each lane gathers its bytes with v_perm.
+// operand order (as the forward's quantisers write them, or k_arrange_scales; one
+// 8-byte LDS read per lane and tile) or in the quantiser's layout, from which each lane
+// gathers its bytes with v_perm.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,8 +94,9 @@ constexpr int BR = 32 * NW;  // queries per workgroup
 //  K scales [4 i + t] dwords: the d/32 scale bytes of key kappa(t, i)
 //  V codes  [ct][c][l]: unit (ct, c, l) = keys 64c + 32(l/32) .. +31 of channel 32ct + l%32
 //  V scales [NCT i + ct] dwords: the 4 scale bytes (one per 32-key block) of channel 32ct + i
-// or, when the scales come pre-arranged (the forward's own workspace, written by
-// k_arrange_scales), the two scale regions hold exactly the lanes' MFMA scale operands:
+// or, when the scales come pre-arranged (the forward's own workspace, written in that
+// order by its quantisers; mxattn_arrange_scales for caller-quantised operands), the two
+// scale regions hold exactly the lanes' MFMA scale operands:
 //  K scales [2 lane + s] dwords: byte t = scale of key kappa(t, lane%32), d-block 2s + lane/32
 //  V scales [2 lane + c] dwords: byte ct = scale of channel 32ct + lane%32, key block 2c + lane/32
 // so a lane loads its operands with one 8-byte read and no byte gathers.
@@ -301,7 +303,6 @@ __device__ __forceinline__ void soft_exp(const v16f& xa, const v16f& xb, float y
   }
 }
 
-// O~^T += V^^T P^^T for 64-key chunk c, plus (PNQ) the row sum of the same P^ as a ones MFMA.
 // O~^T += V^^T P^^T for the 64-key chunk c (its V^ fragments read here, so only one
 // chunk's occupy registers), plus with PNQ the row sum of the same P^: r = its total.
 template <int D, bool PNQ>
