@@ -57,3 +57,29 @@ def test_quant_error_replays_clear_their_sums():
         g.replay()
         torch.cuda.synchronize()
         torch.testing.assert_close(sums, ref, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("d,Nkv", [(128, 1000), (64, 300)])
+def test_noalloc_forward_replays_on_new_inputs(d, Nkv):
+    """mxattn_forward_noalloc is the entry point for callers that cannot allocate, graph
+    capture among them: its captured call, replayed on new inputs copied into the captured
+    buffers, is bitwise the allocating mxattn_forward on those inputs every time."""
+    torch, mx = require_gpu()
+    B, H, Nq = 1, 2, 257
+    scale = float(1.0 / np.sqrt(d))
+    gen = torch.Generator(device="cuda").manual_seed(d + Nkv)
+    sets = [tuple(torch.randn((B, H, n, d), generator=gen, device="cuda").to(torch.bfloat16)
+                  for n in (Nq, Nkv, Nkv)) for _ in range(3)]
+    q, k, v = (t.clone() for t in sets[0])
+    out = torch.empty_like(q)
+    g = _capture(torch, lambda: mx.mxattn_forward_noalloc(q, k, v, scale, out=out))
+    for i, (qs, ks, vs) in enumerate(sets[1:] + sets[:1] + sets[1:2]):
+        q.copy_(qs)
+        k.copy_(ks)
+        v.copy_(vs)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        ref = mx.mxattn_forward(qs, ks, vs, scale)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
