@@ -637,6 +637,8 @@ __global__ __launch_bounds__(NT, 3) void k_attn(AttnArgs a, Rule prule, int qtil
   const int nfull = nkv / BC;  // tiles with no padded key
 
   if (tid < 4) lones[tid] = 0x22222222u;
+  // the first tile's barrier publishes it; that barrier does not wait for LDS writes itself
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
   // Wait for this wave's DMAs of tile j (those of tile j + 1 may stay in flight);
   // the barrier then makes every wave's DMAs of tile j visible and guarantees that

@@ -113,6 +113,22 @@ def _dma_step(tk, pending):
     return pending, int(op.startswith("ds_read") and pending)
 
 
+def _lds_write_step(tk, pending):
+    op = tk[0]
+    if op.startswith("ds_write"):
+        return True, 0
+    if op == "s_waitcnt" and any(a.rstrip(",") == "lgkmcnt(0)" for a in tk[1:]):
+        return False, 0
+    return pending, int(op == "s_barrier" and pending)
+
+
+def barrier_with_lds_write_in_flight(asm: str, name_re: str = r"_Z\w*k_(?:attn|quant)\w*") -> dict:
+    """{kernel symbol: number of s_barrier reachable while an LDS write issued since the last
+    lgkmcnt(0) wait may be in flight}.  s_barrier itself does not wait for the wave's
+    memory operations on this part, so another wave may read LDS before such a write lands."""
+    return {name: _flagged(blocks, _lds_write_step) for name, blocks in _kernel_blocks(asm, name_re)}
+
+
 def lds_read_with_dma_in_flight(asm: str, name_re: str = r"_Z\w*k_quant\w*") -> dict:
     """{kernel symbol: number of LDS reads reachable while a global->LDS DMA issued since
     the last vmcnt(0) wait may still be in flight}."""
@@ -183,6 +199,28 @@ def test_no_quantiser_reads_lds_while_its_dma_may_be_in_flight(tmp_path):
     res = lds_read_with_dma_in_flight(_compile(tmp_path, "quantize.hip"))
     # Hadamard (d x input width x plain/error/arranged), token-axis and the fused K/V kernel
     assert sum("k_quant_hadamard" in k for k in res) == 12 and sum("k_quant_kv" in k for k in res) == 4
+    assert all(n == 0 for n in res.values()), res
+
+
+def test_checker_flags_a_barrier_before_an_lds_write_lands():
+    asm = "\n".join([
+        "_ZN6mxattn6k_attnILi128EEEvv:",
+        "  ds_write_b32 v0, v1",
+        "  s_cbranch_scc1 .LBB0_2",
+        "  s_waitcnt lgkmcnt(0)",
+        "  s_barrier",
+        ".LBB0_2:",
+        "  s_barrier",                            # reached from the branch with the write in flight
+        "  s_endpgm",
+        ".Lfunc_end0:",
+    ])
+    assert list(barrier_with_lds_write_in_flight(asm).values()) == [1]
+
+
+def test_no_barrier_passes_an_lds_write_in_flight(tmp_path):
+    res = barrier_with_lds_write_in_flight(_compile(tmp_path, "attention.hip"))
+    res.update(barrier_with_lds_write_in_flight(_compile(tmp_path, "quantize.hip")))
+    assert sum("k_attn" in k for k in res) >= 8
     assert all(n == 0 for n in res.values()), res
 
 
