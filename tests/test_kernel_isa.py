@@ -200,6 +200,9 @@ def test_no_quantiser_reads_lds_while_its_dma_may_be_in_flight(tmp_path):
     # Hadamard (d x input width x plain/error/arranged), token-axis and the fused K/V kernel
     assert sum("k_quant_hadamard" in k for k in res) == 12 and sum("k_quant_kv" in k for k in res) == 4
     assert all(n == 0 for n in res.values()), res
+    # the bandwidth probe that reads its DMA'd LDS back (copy mode) obeys the same order
+    probes = lds_read_with_dma_in_flight(_compile(tmp_path, "probes.hip"), r"_Z\w*k_stream_dma\w*")
+    assert len(probes) == 2 and all(n == 0 for n in probes.values()), probes
 
 
 def test_checker_flags_a_barrier_before_an_lds_write_lands():
