@@ -377,7 +377,7 @@ def main():
     }
     del qc, qs, kc, ks, vc, vs, ksa, vsa
 
-    if not args.no_denominators:
+    def denominators():
         from mxfp4_bit_attention_amd import probes
         den = probes.measure(torch, dev)
         result["denominators"] = den
@@ -389,7 +389,7 @@ def main():
         roofline["alu_floor"] = fl
         roofline["tile_mix"] = tile_mix_ceiling(den, w.d, achieved)
 
-    if not args.no_quantize_pass:
+    def quantize_pass():
         qw = synth.QUANT_720P
         # the seeded host law, as the whole-tensor parity test draws it
         xh = synth.quant_tensor_bf16(qw, threads=min(16, len(os.sched_getaffinity(0))))
@@ -423,22 +423,34 @@ def main():
             if "stream_model_us" in qp:
                 qp[name]["frac_of_stream_model"] = round(qp["stream_model_us"] / (ms * 1e3), 4)
         result["quantize_pass"] = qp
-        del x, c, s
 
-    if not args.no_extras:
+    def other_shapes():
         result.update(extras(torch, mx, w, q, k, v, out, ws, stream))
         if "denominators" in result:
             d64 = result["other_shapes"]["d64"]
             d64["tile_mix"] = tile_mix_ceiling(result["denominators"], 64, d64["TFLOPs"])
-    del q, k, v, out, ws
 
-    if not args.no_cpu_baseline:
+    def cpu_baselines():
         result["cpu_baseline"] = cpu_baseline(w)
         hy = synth.HUNYUAN_720P
         result["cpu_baseline_other"] = {
             synth.WAN_480P.name: cpu_baseline(synth.WAN_480P, rows=512),
             hy.name + " (text rows)": cpu_baseline(hy, rows=hy.text_rows, row_start=hy.N - hy.text_rows),
         }
+
+    # the sections after the headline figures: a Python-level failure in one is reported in
+    # the line (as <section>_error) instead of losing the figures already measured
+    for skip, name, fn in ((args.no_denominators, "denominators", denominators),
+                           (args.no_quantize_pass, "quantize_pass", quantize_pass),
+                           (args.no_extras, "other_shapes", other_shapes),
+                           (args.no_cpu_baseline, "cpu_baseline", cpu_baselines)):
+        if skip:
+            continue
+        try:
+            fn()
+        except Exception as e:  # reported in the line and on stderr, not swallowed
+            result[name + "_error"] = f"{type(e).__name__}: {e}"[:400]
+            print(f"bench.py: the {name} section failed: {e!r}", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
 
 
