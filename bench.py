@@ -160,6 +160,12 @@ def tile_mix_ceiling(den: dict, d: int, achieved: float) -> dict:
     for k in ("valu_only_cycles", "mfma_only_cycles", "mfma_hidden"):
         if k in m:
             out[k] = m[k]
+    if "random_operands" in m:
+        # the same mix with pseudo-random MFMA operands, at the clock it sustains then
+        r = m["random_operands"]
+        rp = 4.0 * 32 * 128 * d * simds * r["clock_MHz"] * 1e6 / r["cycles_per_trip_per_wave"] / 1e12
+        out["random_operands"] = {"cycles_per_wave_tile": r["cycles_per_trip_per_wave"], "clock_MHz": r["clock_MHz"],
+                                  "peak_TFLOPs": round(rp, 1), "frac": round(achieved / rp, 4)}
     return out
 
 
@@ -384,6 +390,11 @@ def main():
         mf = den["mfma_fp4_32x32x64"]["TFLOPs"]
         roofline["peak_measured"] = mf
         roofline["frac_measured"] = round(achieved / mf, 4)
+        # the same MFMA loop on pseudo-random operands: the rate the part sustains on data that
+        # toggles as real operands do
+        mfr = den["mfma_fp4_32x32x64_random_operands"]["TFLOPs"]
+        roofline["peak_measured_random_operands"] = mfr
+        roofline["frac_measured_random_operands"] = round(achieved / mfr, 4)
         fl = alu_floor(den, w.d)
         fl["frac"] = round(achieved / fl["peak_TFLOPs"], 4)
         roofline["alu_floor"] = fl

@@ -31,19 +31,46 @@ __device__ __forceinline__ void record(unsigned long long* st, unsigned long lon
   }
 }
 
+// MFMA operands: with RAND, four sets of pseudo-random fp4 codes per lane (a counter hash),
+// one per accumulator chain, so that successive MFMAs see different bits as they do on real
+// data (the part's clock under load depends on how much the operands toggle); otherwise one
+// constant pattern.
+struct Operands {
+  v8i a[4], b[4];
+};
+template <bool RAND>
+__device__ __forceinline__ Operands operands(int code) {
+  Operands o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t h = (threadIdx.x + 256u * blockIdx.x) * 0x9E3779B9u + (uint32_t)k * 0x85EBCA6Bu;
+    int w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h ^= h >> 15;
+      h *= 0x2C1B3C6Du;
+      h ^= h >> 12;
+      w[e] = RAND ? (int)h : code;
+    }
+    o.a[k] = v8i{w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+    o.b[k] = v8i{RAND ? w[4] : code ^ (int)threadIdx.x, w[5], w[6], w[7], 0, 0, 0, 0};
+  }
+  return o;
+}
+
 // Four independent accumulator chains of 32x32x64 fp4 x fp4 MFMAs (E8M0 scales), issued
 // back to back: 4 * iters MFMAs per wave, 2 * 32 * 32 * 64 flop each.
+template <bool RAND>
 __global__ __launch_bounds__(256) void k_mfma_fp4(int64_t iters, int code, int scale, unsigned long long* st) {
-  const v8i a = {code, code, code, code, 0, 0, 0, 0};
-  const v8i b = {code ^ (int)threadIdx.x, code, code, code, 0, 0, 0, 0};
+  const Operands o = operands<RAND>(code);
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
   const unsigned long long t0 = __builtin_amdgcn_s_memtime();
   const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
   for (int64_t i = 0; i < iters; ++i) {
-    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 4, 4, 0, scale, 0, scale);
-    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 4, 4, 0, scale, 0, scale);
-    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 4, 4, 0, scale, 0, scale);
-    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 4, 4, 0, scale, 0, scale);
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[0], o.b[0], c0, 4, 4, 0, scale, 0, scale);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[1], o.b[1], c1, 4, 4, 0, scale, 0, scale);
+    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[2], o.b[2], c2, 4, 4, 0, scale, 0, scale);
+    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[3], o.b[3], c3, 4, 4, 0, scale, 0, scale);
   }
   float keep = 0.0f;
 #pragma unroll
@@ -102,10 +129,9 @@ __global__ __launch_bounds__(256) void k_valu(int64_t iters, float seed, unsigne
 // on its own.  VALU = false keeps only the MFMAs, NMFMA = 0 only the vector instructions:
 // the two parts alone against the whole show how much of the MFMA time the vector work
 // hides.
-template <int NMFMA, bool VALU = true>
+template <int NMFMA, bool VALU = true, bool RAND = false>
 __global__ __launch_bounds__(256, 3) void k_mix(int64_t iters, int code, unsigned long long* st) {
-  const v8i a = {code, code, code, code, 0, 0, 0, 0};
-  const v8i b = {code ^ (int)threadIdx.x, code, code, code, 0, 0, 0, 0};
+  const Operands o = operands<RAND>(code);
   v16f c[4] = {};
   float x[8], y[8], z[8];
   uint32_t r[8];
@@ -121,7 +147,8 @@ __global__ __launch_bounds__(256, 3) void k_mix(int64_t iters, int code, unsigne
   const unsigned long long w0 = __builtin_amdgcn_s_memrealtime();
   for (int64_t i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int k = 0; k < NMFMA; ++k) c[k & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[k & 3], 4, 4, 0, 127, 0, 127);
+    for (int k = 0; k < NMFMA; ++k)
+      c[k & 3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(o.a[k & 3], o.b[k & 3], c[k & 3], 4, 4, 0, 127, 0, 127);
     if constexpr (VALU) {
       // the max3 operands change every step, so no two of them can be folded
 #pragma unroll
@@ -245,11 +272,15 @@ int32_t mxprobe_wall_clock_khz(void) {
 
 // Returns 0, -1 for bad arguments, -4 for a launch error.  waves_per_simd: 1..8 (one
 // 4-wave workgroup per compute unit and wave per SIMD).
-int32_t mxprobe_mfma_fp4(int64_t iters, int32_t waves_per_simd, uint64_t* stats, void* stream) {
+int32_t mxprobe_mfma_fp4(int64_t iters, int32_t waves_per_simd, int32_t random_operands, uint64_t* stats,
+                         void* stream) {
   const int cus = cu_count();
   if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 8 || !stats || cus < 1) return -1;
-  hipLaunchKernelGGL(k_mfma_fp4, dim3(cus * waves_per_simd), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
-                     0x22222222, 127, reinterpret_cast<unsigned long long*>(stats));
+  const dim3 g(cus * waves_per_simd), b(256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
+  if (random_operands) hipLaunchKernelGGL(k_mfma_fp4<true>, g, b, 0, s, iters, 0x22222222, 127, st);
+  else hipLaunchKernelGGL(k_mfma_fp4<false>, g, b, 0, s, iters, 0x22222222, 127, st);
   return status(hipGetLastError());
 }
 
@@ -273,14 +304,17 @@ int32_t mxprobe_valu(int32_t kind, int64_t iters, int32_t waves_per_simd, uint64
 }
 
 // The attention tile's instruction mix (k_mix) for head dimension d (128 or 64), three
-// waves per SIMD.  part: 0 the whole mix, 1 its vector instructions only, 2 its MFMAs only.
+// waves per SIMD.  part: 0 the whole mix, 1 its vector instructions only, 2 its MFMAs only,
+// 3 the whole mix with pseudo-random MFMA operands (d = 128 only).
 int32_t mxprobe_mix(int64_t iters, int32_t d, int32_t part, uint64_t* stats, void* stream) {
   const int cus = cu_count();
-  if (iters < 1 || !stats || cus < 1 || (d != 128 && d != 64) || part < 0 || part > 2) return -1;
+  if (iters < 1 || !stats || cus < 1 || (d != 128 && d != 64) || part < 0 || part > 3 || (part == 3 && d != 128))
+    return -1;
   unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
   const dim3 g(cus * 3), b(256);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (part == 1) hipLaunchKernelGGL((k_mix<0, true>), g, b, 0, s, iters, 0x22222222, st);
+  if (part == 3) hipLaunchKernelGGL((k_mix<18, true, true>), g, b, 0, s, iters, 0x22222222, st);
+  else if (part == 1) hipLaunchKernelGGL((k_mix<0, true>), g, b, 0, s, iters, 0x22222222, st);
   else if (d == 128 && part == 0) hipLaunchKernelGGL((k_mix<18, true>), g, b, 0, s, iters, 0x22222222, st);
   else if (d == 128) hipLaunchKernelGGL((k_mix<18, false>), g, b, 0, s, iters, 0x22222222, st);
   else if (part == 0) hipLaunchKernelGGL((k_mix<10, true>), g, b, 0, s, iters, 0x22222222, st);

@@ -1,7 +1,9 @@
 """Measured roofline denominators (ctypes binding of libmxattn_probes.so).
 
 The microbenchmarks of csrc/probes.hip, run on the current GPU: the dense fp4
-block-scaled MFMA rate (32x32x64, E8M0 scales) with the core clock it sustains, the
+block-scaled MFMA rate (32x32x64, E8M0 scales) with the core clock it sustains, on one
+constant operand pattern and on pseudo-random operands (the clock the part sustains
+depends on how much the operands toggle), the
 issue rate of each vector instruction the attention kernel's softmax uses
 (v_exp_f32, v_cvt_scalef32_pk_fp4_f32, v_fma_f32, v_max3_f32) in cycles per wave64
 instruction per SIMD, whether exponentials and FMAs overlap, and HBM streaming read
@@ -34,7 +36,7 @@ def _load():
     lib.mxprobe_cu_count.restype = i32
     lib.mxprobe_wall_clock_khz.restype = i32
     lib.mxprobe_mfma_fp4.restype = i32
-    lib.mxprobe_mfma_fp4.argtypes = [i64, i32, vp, vp]
+    lib.mxprobe_mfma_fp4.argtypes = [i64, i32, i32, vp, vp]
     lib.mxprobe_valu.restype = i32
     lib.mxprobe_valu.argtypes = [i32, i64, i32, vp, vp]
     lib.mxprobe_hbm_read.restype = i32
@@ -88,18 +90,20 @@ def measure(torch, device=None, hbm_bytes: int = 1 << 31) -> dict:
     simds = 4 * cus
     out = {"compute_units": cus, "wall_clock_kHz": wall_khz}
 
-    # --- fp4 MFMA, one and two waves per SIMD (four independent accumulator chains each)
-    best = None
-    for wps in (1, 2):
-        iters = 50000 // wps
-        ms, clk = _run(torch, lambda st: lib.mxprobe_mfma_fp4(iters, wps, st, sp), stream, dev, wall_khz)
-        per_simd = wps * iters * MFMA_PER_TRIP
-        row = {"waves_per_simd": wps, "TFLOPs": round(simds * per_simd * MFMA_FLOP / (ms * 1e-3) / 1e12, 1),
-               "clock_MHz": round(clk, 1), "cycles_per_mfma_per_simd": round(ms * 1e-3 * clk * 1e6 / per_simd, 2),
-               "ms": round(ms, 3)}
-        if best is None or row["TFLOPs"] > best["TFLOPs"]:
-            best = row
-    out["mfma_fp4_32x32x64"] = best
+    # --- fp4 MFMA, one and two waves per SIMD (four independent accumulator chains each), with
+    # one constant operand pattern and with pseudo-random operands (real data's toggling)
+    for rnd, key in ((0, "mfma_fp4_32x32x64"), (1, "mfma_fp4_32x32x64_random_operands")):
+        best = None
+        for wps in (1, 2):
+            iters = 50000 // wps
+            ms, clk = _run(torch, lambda st: lib.mxprobe_mfma_fp4(iters, wps, rnd, st, sp), stream, dev, wall_khz)
+            per_simd = wps * iters * MFMA_PER_TRIP
+            row = {"waves_per_simd": wps, "TFLOPs": round(simds * per_simd * MFMA_FLOP / (ms * 1e-3) / 1e12, 1),
+                   "clock_MHz": round(clk, 1),
+                   "cycles_per_mfma_per_simd": round(ms * 1e-3 * clk * 1e6 / per_simd, 2), "ms": round(ms, 3)}
+            if best is None or row["TFLOPs"] > best["TFLOPs"]:
+                best = row
+        out[key] = best
 
     # --- vector instructions: cycles per wave64 instruction per SIMD, 1 and 3 waves per SIMD
     def valu(kind, wps, it=6000):
@@ -137,6 +141,9 @@ def measure(torch, device=None, hbm_bytes: int = 1 << 31) -> dict:
             "clock_MHz": round(clk, 1), "ms": round(ms, 3)}
     _, _, valu_only = mix(128, 1)
     _, _, mfma_only = mix(128, 2)
+    _, clk_rand, cyc_rand = mix(128, 3)
+    out["attention_tile_mix"]["random_operands"] = {"cycles_per_trip_per_wave": round(cyc_rand, 1),
+                                                    "clock_MHz": round(clk_rand, 1)}
     whole = out["attention_tile_mix"]["cycles_per_trip_per_wave"]
     out["attention_tile_mix"]["valu_only_cycles"] = round(valu_only, 1)
     out["attention_tile_mix"]["mfma_only_cycles"] = round(mfma_only, 1)
