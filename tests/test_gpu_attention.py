@@ -174,10 +174,11 @@ def test_mid_size_bf16_all_rows():
         assert err < REL_L2, f"head {h}: rel-L2 {err:.2e}"
 
 
-def _full_size_case(w, rows_per_head=32):
+def _full_size_case(w, rows_per_head=32, rule="uos"):
     """Full-size workload on the device; heads 0 and H-1 come from the seeded host
     generator (the oracle compares sampled rows of those), the other heads are
     filled on the device with the same Gaussian law."""
+    gpu_rule, ora_rule = RULES[rule]
     torch, mx = require_gpu()
     gen = torch.Generator(device="cuda").manual_seed(w.seed)
     shape = (w.B, w.H, w.N, w.d)
@@ -190,7 +191,7 @@ def _full_size_case(w, rows_per_head=32):
             host[tid, h] = x
             dev[tid][0, h] = to_device(x, "bf16")
     scale = float(np.float32(w.softmax_scale))
-    O = mx.mxattn_forward(*dev, scale, hadamard=True, pnq=True, rule="uos")
+    O = mx.mxattn_forward(*dev, scale, hadamard=True, pnq=True, rule=gpu_rule)
     torch.cuda.synchronize()
     Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(w.N)
     rng = np.random.default_rng(w.seed)
@@ -199,12 +200,12 @@ def _full_size_case(w, rows_per_head=32):
         rows = np.unique(np.concatenate([rows, [0, w.N - 1]]))
         Og = O[0, h, torch.from_numpy(rows).cuda()].float().cpu().numpy()
         # quantisation is row-local, so quantising only the sampled query rows is exact
-        Qc, Qs = ora.quantize_qk(host[synth.Q_ID, h][rows], mxfp4.UOS, True)
-        Kc, Ks = ora.quantize_qk(host[synth.K_ID, h], mxfp4.UOS, True)
-        Vc, Vs = ora.quantize_v(host[synth.V_ID, h], mxfp4.UOS, P)
-        Oo = ora.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, w.N, scale, True, mxfp4.UOS, Bc)
+        Qc, Qs = ora.quantize_qk(host[synth.Q_ID, h][rows], ora_rule, True)
+        Kc, Ks = ora.quantize_qk(host[synth.K_ID, h], ora_rule, True)
+        Vc, Vs = ora.quantize_v(host[synth.V_ID, h], ora_rule, P)
+        Oo = ora.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, w.N, scale, True, ora_rule, Bc)
         err = rel_l2(Og, Oo)
-        assert err < REL_L2, f"{w.name} head {h}: rel-L2 {err:.2e}"
+        assert err < REL_L2, f"{w.name} {rule} head {h}: rel-L2 {err:.2e}"
 
 
 def test_full_size_wan480p_sampled_rows():
@@ -213,6 +214,13 @@ def test_full_size_wan480p_sampled_rows():
 
 def test_full_size_wan720p_sampled_rows():
     _full_size_case(synth.WAN_720P)
+
+
+@pytest.mark.parametrize("rule", ["ocp", "tfs"])
+def test_full_size_wan720p_sampled_rows_other_rules(rule):
+    """The benchmark's rule ablation runs the full Wan2.2-720p step under every rule; the
+    OCP floor rule and TFS (q = 6) against the oracle at that size too."""
+    _full_size_case(synth.WAN_720P, rows_per_head=16, rule=rule)
 
 
 def test_full_size_hunyuan720p_sampled_rows():
