@@ -174,7 +174,7 @@ def test_mid_size_bf16_all_rows():
         assert err < REL_L2, f"head {h}: rel-L2 {err:.2e}"
 
 
-def _full_size_case(w, rows_per_head=32, rule="uos"):
+def _full_size_case(w, rows_per_head=32, rule="uos", pnq=True):
     """Full-size workload on the device; heads 0 and H-1 come from the seeded host
     generator (the oracle compares sampled rows of those), the other heads are
     filled on the device with the same Gaussian law."""
@@ -191,7 +191,7 @@ def _full_size_case(w, rows_per_head=32, rule="uos"):
             host[tid, h] = x
             dev[tid][0, h] = to_device(x, "bf16")
     scale = float(np.float32(w.softmax_scale))
-    O = mx.mxattn_forward(*dev, scale, hadamard=True, pnq=True, rule=gpu_rule)
+    O = mx.mxattn_forward(*dev, scale, hadamard=True, pnq=pnq, rule=gpu_rule)
     torch.cuda.synchronize()
     Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(w.N)
     rng = np.random.default_rng(w.seed)
@@ -203,7 +203,7 @@ def _full_size_case(w, rows_per_head=32, rule="uos"):
         Qc, Qs = ora.quantize_qk(host[synth.Q_ID, h][rows], ora_rule, True)
         Kc, Ks = ora.quantize_qk(host[synth.K_ID, h], ora_rule, True)
         Vc, Vs = ora.quantize_v(host[synth.V_ID, h], ora_rule, P)
-        Oo = ora.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, w.N, scale, True, ora_rule, Bc)
+        Oo = ora.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, w.N, scale, pnq, ora_rule, Bc)
         err = rel_l2(Og, Oo)
         assert err < REL_L2, f"{w.name} {rule} head {h}: rel-L2 {err:.2e}"
 
@@ -221,6 +221,11 @@ def test_full_size_wan720p_sampled_rows_other_rules(rule):
     """The benchmark's rule ablation runs the full Wan2.2-720p step under every rule; the
     OCP floor rule and TFS (q = 6) against the oracle at that size too."""
     _full_size_case(synth.WAN_720P, rows_per_head=16, rule=rule)
+
+
+def test_full_size_wan720p_sampled_rows_direct_placement():
+    """Direct placement (pnq = 0: the row sum from the unquantised P~) at full size."""
+    _full_size_case(synth.WAN_720P, rows_per_head=16, pnq=False)
 
 
 def test_full_size_hunyuan720p_sampled_rows():
