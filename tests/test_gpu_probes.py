@@ -23,7 +23,8 @@ def test_probe_figures_are_physical():
         # one 32x32x64 fp4 MFMA keeps a SIMD's matrix pipe busy for 32 cycles
         assert 30 < mf["cycles_per_mfma_per_simd"] < 40, key
     for name, row in den["valu_cycles_per_instruction_per_simd"].items():
-        assert 1.5 < row["cycles_3w"] <= row["cycles_1w"] < 16, name
+        # three waves per SIMD issue at least as fast as one (3% allowed for timing noise)
+        assert 1.5 < row["cycles_3w"] <= 1.03 * row["cycles_1w"] and row["cycles_1w"] < 16, name
         assert 1000 < row["clock_MHz_3w"] < 2600, name
     for key, nm in (("attention_tile_mix", 18), ("attention_tile_mix_d64", 10)):
         m = den[key]
