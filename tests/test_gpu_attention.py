@@ -238,6 +238,35 @@ def test_full_size_d64_sampled_rows():
     _full_size_case(w)
 
 
+@pytest.mark.parametrize("B,H,Nq,Nkv", [(2, 20, 75_600, 75_600), (1, 40, 75_600, 512), (1, 40, 2048, 2048),
+                                        (1, 40, 8192, 8192)])
+def test_benchmark_extra_shapes_sampled_rows(B, H, Nq, Nkv):
+    """The further shapes the benchmark times (B = 2 x H = 20, a 512-key cross-attention
+    shape, 2,048 and 8,192 tokens), on the same seeded unit-Gaussian bf16 inputs and through
+    the same call: sampled rows of the first and the last head against the oracle."""
+    torch, mx = require_gpu()
+    d = 128
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    mk = lambda n: torch.randn((B, H, n, d), generator=gen, device="cuda").to(torch.bfloat16)
+    q, k, v = mk(Nq), mk(Nkv), mk(Nkv)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    O = mx.mxattn_forward(q, k, v, scale, hadamard=True, pnq=True, rule="uos")
+    torch.cuda.synchronize()
+    gpu_rule, ora_rule = RULES["uos"]
+    Bc, P = mx.mxattn_kv_tile(), mx.mxattn_padded_tokens(Nkv)
+    rng = np.random.default_rng(1000 * B + Nkv)
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        rows = np.unique(np.concatenate([rng.choice(Nq, 16, replace=False), [0, Nq - 1]]))
+        host = lambda t: t[b, h].float().cpu().numpy()
+        Og = O[b, h, torch.from_numpy(rows).cuda()].float().cpu().numpy()
+        Qc, Qs = ora.quantize_qk(host(q)[rows], ora_rule, True)
+        Kc, Ks = ora.quantize_qk(host(k), ora_rule, True)
+        Vc, Vs = ora.quantize_v(host(v), ora_rule, P)
+        Oo = ora.flash_attention_mx(Qc, Qs, Kc, Ks, Vc, Vs, Nkv, scale, True, ora_rule, Bc)
+        err = rel_l2(Og, Oo)
+        assert err < REL_L2, f"B={B} H={H} Nq={Nq} Nkv={Nkv} head ({b}, {h}): rel-L2 {err:.2e}"
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_repeatable_bitwise(d):
     """The forward ten times, and the quantised entry with its P^ dump ten times, on the
