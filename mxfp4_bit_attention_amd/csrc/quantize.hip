@@ -5,6 +5,9 @@
 //  k_quant_last     : block quantisation along the last axis, no rotation.
 //  k_quant_rows     : block quantisation down the rows (V along tokens), written
 //                     transposed so each channel's kv codes are contiguous.
+//  k_quant_kv       : the forward's K (rotation + quantisation) and V (token axis)
+//                     in one launch, for K and V small enough that a launch's ramp
+//                     is a visible share of the step.
 //
 // Method: Pith review of MXAttention, Axiom ledger (axiom 1: 32-element E2M1
 // blocks with one E8M0 scale; Hadamard rotation on Q/K, sec. 4.3) and Figure 3
